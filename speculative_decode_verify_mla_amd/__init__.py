@@ -1,0 +1,15 @@
+"""MLA tree-verify attention for MI355X (gfx950).
+
+The compute lives in ``libmla_verify.so`` (hand-written HIP kernels behind a C
+ABI, declared in ``include/mla_verify.h``). This package only marshals torch
+tensors into that ABI; ``synth`` draws seeded synthetic inputs.
+"""
+from .binding import (  # noqa: F401
+    MlaError,
+    load_library,
+    plan,
+    sparse_attn,
+    strerror,
+    verify_attn,
+    workspace_bytes,
+)

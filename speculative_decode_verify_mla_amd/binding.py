@@ -1,0 +1,213 @@
+"""ctypes binding of libmla_verify.so (include/mla_verify.h).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels. Tensors are torch device tensors; the call is enqueued on the
+current torch stream (or the one given) and returns without synchronising.
+There is no fallback: if the library is missing or fails to load, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_verify.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID = -1
+MLA_ERR_WORKSPACE = -2
+MLA_ERR_HIP = -3
+MLA_ERR_UNSUPPORTED = -4
+
+PHASE_ALL = 0
+PHASE_PARTIAL = 1
+PHASE_COMBINE = 2
+
+EXPORTED = (
+    "mla_verify_plan",
+    "mla_verify_workspace_bytes",
+    "mla_verify_attn",
+    "mla_sparse_attn",
+    "mla_verify_strerror",
+)
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32),
+        ("kv_seq_stride", ctypes.c_int64),
+        ("kv_rows", ctypes.c_int64),
+        ("topk", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("phase", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class MlaPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("num_splits", ctypes.c_int32),
+        ("chunk_tiles", ctypes.c_int32),
+        ("row_blocks", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32),
+        ("rows_per_group", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: Optional[str] = None):
+    """Load (once) and return the ctypes handle of libmla_verify.so."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(
+                f"{p} is missing: build it with `python -m speculative_decode_verify_mla_amd.build`")
+        lib = ctypes.CDLL(p)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        dims_p = ctypes.POINTER(MlaDims)
+        lib.mla_verify_plan.argtypes = [dims_p, i32, ctypes.POINTER(MlaPlanInfo)]
+        lib.mla_verify_plan.restype = i32
+        lib.mla_verify_workspace_bytes.argtypes = [dims_p, i32]
+        lib.mla_verify_workspace_bytes.restype = sz
+        common = [dims_p, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+        lib.mla_verify_attn.argtypes = common
+        lib.mla_verify_attn.restype = i32
+        lib.mla_sparse_attn.argtypes = common
+        lib.mla_sparse_attn.restype = i32
+        lib.mla_verify_strerror.argtypes = [i32]
+        lib.mla_verify_strerror.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def strerror(code: int) -> str:
+    try:
+        return load_library().mla_verify_strerror(int(code)).decode()
+    except Exception:  # library missing: still describe the code
+        return {0: "success", -1: "invalid argument", -2: "workspace missing or too small",
+                -3: "HIP runtime or launch failure", -4: "device is not gfx950"}.get(code, "unknown")
+
+
+def make_dims(*, batch, num_q, num_heads, max_kv_len, kv_rows, kv_seq_stride=0, page_size=0,
+              max_pages=0, topk=0, num_splits=0, phase=PHASE_ALL) -> MlaDims:
+    return MlaDims(batch=batch, num_q=num_q, num_heads=num_heads, page_size=page_size,
+                   max_pages=max_pages, max_kv_len=max_kv_len, kv_seq_stride=kv_seq_stride,
+                   kv_rows=kv_rows, topk=topk, num_splits=num_splits, phase=phase, reserved=0)
+
+
+def plan(dims: MlaDims, sparse: bool = False) -> MlaPlanInfo:
+    info = MlaPlanInfo()
+    rc = load_library().mla_verify_plan(ctypes.byref(dims), int(bool(sparse)), ctypes.byref(info))
+    if rc != MLA_OK:
+        raise MlaError(rc, "mla_verify_plan")
+    return info
+
+
+def workspace_bytes(dims: MlaDims, sparse: bool = False) -> int:
+    return int(load_library().mla_verify_workspace_bytes(ctypes.byref(dims), int(bool(sparse))))
+
+
+# --------------------------------------------------------------------------
+# torch-tensor front end
+# --------------------------------------------------------------------------
+_ws_cache = {}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _workspace(device, nbytes: int):
+    import torch
+
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _dims_from(q_lat, c_kv, kv_lens, *, max_kv_len, kv_seq_stride, page_table, page_size, topk,
+               num_splits, phase) -> MlaDims:
+    B, T, H, dl = q_lat.shape
+    if dl != 512:
+        raise ValueError("q_lat must be [B, T, H, 512]")
+    return make_dims(batch=B, num_q=T, num_heads=H, max_kv_len=int(max_kv_len),
+                     kv_rows=int(c_kv.shape[0]), kv_seq_stride=int(kv_seq_stride),
+                     page_size=int(page_size) if page_table is not None else 0,
+                     max_pages=int(page_table.shape[1]) if page_table is not None else 0,
+                     topk=int(topk), num_splits=int(num_splits), phase=int(phase))
+
+
+def _call(fn_name, dims, sparse, q_lat, q_rope, c_kv, k_rope, page_table, mask_or_idx, kv_lens,
+          scale, out, lse, workspace, stream):
+    import torch
+
+    lib = load_library()
+    if workspace is None:
+        info = plan(dims, sparse)
+        workspace = _workspace(q_lat.device, int(info.workspace_bytes))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q_lat.device)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    rc = getattr(lib, fn_name)(ctypes.byref(dims), _ptr(q_lat), _ptr(q_rope), _ptr(c_kv),
+                               _ptr(k_rope), _ptr(page_table), _ptr(mask_or_idx), _ptr(kv_lens),
+                               ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                               ctypes.c_size_t(ws_bytes), sptr)
+    if rc != MLA_OK:
+        raise MlaError(rc, fn_name)
+
+
+def _as_u16(t):
+    import torch
+
+    return t.view(torch.uint16) if t.dtype == torch.bfloat16 else t
+
+
+def verify_attn(q_lat, q_rope, c_kv, k_rope, page_table, tree_mask, kv_lens, scale, out, lse, *,
+                max_kv_len: int, kv_seq_stride: int = 0, page_size: int = 0, num_splits: int = 0,
+                phase: int = PHASE_ALL, workspace=None, stream=None):
+    """Dense tree-verify attention (mla_verify_attn). bf16 tensors may be torch.bfloat16 or uint16."""
+    dims = _dims_from(q_lat, c_kv, kv_lens, max_kv_len=max_kv_len, kv_seq_stride=kv_seq_stride,
+                      page_table=page_table, page_size=page_size, topk=0, num_splits=num_splits,
+                      phase=phase)
+    _call("mla_verify_attn", dims, False, _as_u16(q_lat), _as_u16(q_rope), _as_u16(c_kv),
+          _as_u16(k_rope), page_table, tree_mask, kv_lens, scale, _as_u16(out), lse, workspace,
+          stream)
+
+
+def sparse_attn(q_lat, q_rope, c_kv, k_rope, page_table, indices, kv_lens, scale, out, lse, *,
+                max_kv_len: int, kv_seq_stride: int = 0, page_size: int = 0, num_splits: int = 0,
+                phase: int = PHASE_ALL, workspace=None, stream=None):
+    """Sparse top-k attention (mla_sparse_attn); indices is int32 [B, T, topk]."""
+    dims = _dims_from(q_lat, c_kv, kv_lens, max_kv_len=max_kv_len, kv_seq_stride=kv_seq_stride,
+                      page_table=page_table, page_size=page_size, topk=int(indices.shape[2]),
+                      num_splits=num_splits, phase=phase)
+    _call("mla_sparse_attn", dims, True, _as_u16(q_lat), _as_u16(q_rope), _as_u16(c_kv),
+          _as_u16(k_rope), page_table, indices, kv_lens, scale, _as_u16(out), lse, workspace,
+          stream)
