@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA tree-verify attention call on one MI355X.
+
+Default workload: long-prefix verify, B=1, H=64 heads, prefix 65,536, T=16
+random draft tree (Dl=512 latent + Dr=64 rope, bf16 N(0,1) synthetic inputs).
+One "step" is one whole verify call (split-KV kernel + log-sum-exp combine)
+with every input already resident in HBM.
+
+Prints ONE JSON line: µs/call (value), achieved HBM GB/s, the split kernel's
+roofline position (its average duration from HIP events on the launch
+stream), and the fp64 CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify-attn µs/call + achieved HBM GB/s (% of peak), H=64, 64k prefix"
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+LATENT_ROW_BYTES = 512 * 2
+ROPE_ROW_BYTES = 64 * 2
+KERNEL_SOURCES = ("speculative_decode_verify_mla_amd/csrc/mla_kernels.hip",
+                  "speculative_decode_verify_mla_amd/csrc/mla_api.hip",
+                  "speculative_decode_verify_mla_amd/csrc/mla_internal.h")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work of one call (each visible KV row counted once per sequence)
+# ---------------------------------------------------------------------------
+def work_model(w):
+    import numpy as np
+
+    B, T, H = w.B, w.T, w.H
+    rows = B * T * H
+    q_bytes = rows * (LATENT_ROW_BYTES + ROPE_ROW_BYTES)
+    out_bytes = rows * LATENT_ROW_BYTES + rows * 4
+    if w.layout == "sparse":
+        kv_rows = sum(len(np.unique(w.indices[b])) for b in range(B))
+        visible = int(np.sum((w.indices >= 0) & (w.indices < w.kv_lens[:, None, None]))) * H
+        meta = w.indices.nbytes + w.kv_lens.nbytes
+        if w.page_table is not None:
+            meta += w.page_table.nbytes
+    else:
+        kv_rows = int(w.kv_lens.sum())
+        prefix = w.kv_lens - T
+        visible = int(sum(H * (prefix[b] * T + int(w.tree_mask[b].sum())) for b in range(B)))
+        meta = w.kv_lens.nbytes + (0 if w.mask_for_kernel is None else w.tree_mask.nbytes)
+        if w.page_table is not None:
+            meta += w.page_table.nbytes
+    kv_bytes = kv_rows * (LATENT_ROW_BYTES + ROPE_ROW_BYTES)
+    flops = 2.0 * visible * (512 + 64 + 512)
+    return dict(kv_bytes=kv_bytes, q_bytes=q_bytes, out_bytes=out_bytes, meta_bytes=meta,
+                total_bytes=kv_bytes + q_bytes + out_bytes + meta, flops=flops,
+                visible_pairs=visible)
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same call."""
+    import numpy as np
+
+    import oracle
+    from speculative_decode_verify_mla_amd.synth import bf16_bits_to_f64
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    q_lat, q_rope = bf16_bits_to_f64(w.q_lat), bf16_bits_to_f64(w.q_rope)
+    c_kv, k_rope = bf16_bits_to_f64(w.c_kv), bf16_bits_to_f64(w.k_rope)
+    tokens = [(b, t) for b in range(w.B) for t in range(w.T)]
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        b, t = tokens[done % len(tokens)]
+        if w.layout == "sparse":
+            sl = (slice(b, b + 1), slice(t, t + 1))
+            oracle.verify_sparse(q_lat[sl], q_rope[sl], c_kv, k_rope, w.kv_lens[b:b + 1],
+                                 w.indices[b:b + 1, t:t + 1], w.scale,
+                                 kv_seq_stride=w.kv_seq_stride,
+                                 page_table=None if w.page_table is None else w.page_table[b:b + 1],
+                                 page_size=w.page_size, row_ids=_rows_of(w, b))
+        else:
+            _token_oracle(oracle, q_lat, q_rope, c_kv, k_rope, w, b, t)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    per_call_us = el / done * len(tokens) * 1e6
+    return dict(value=per_call_us, unit="us/call", cores=int(threads), kind="oracle",
+                sample=f"{done} of the call's {len(tokens)} (sequence, draft-token) groups, "
+                       f"all {w.H} heads each, fp64 numpy oracle, {el:.1f} s wall; "
+                       f"scaled to one whole call")
+
+
+def _rows_of(w, b):
+    """Materialised-row ids as seen from a one-sequence slice (sequence b becomes 0)."""
+    if w.row_ids is None:
+        return None
+    if w.page_table is not None:
+        return w.row_ids
+    return w.row_ids - b * w.kv_seq_stride
+
+
+def _token_oracle(oracle, q_lat, q_rope, c_kv, k_rope, w, b, t):
+    """The oracle's own per-token step: visible positions, gather, attend."""
+    import numpy as np
+
+    mrow = None if w.mask_for_kernel is None else w.tree_mask[b, t]
+    pos = oracle.dense_visible_positions(int(w.kv_lens[b]), w.T, t, mrow)
+    if w.page_table is None:
+        phys = b * w.kv_seq_stride + pos
+    else:
+        phys = w.page_table[b][pos // w.page_size].astype(np.int64) * w.page_size + pos % w.page_size
+    return oracle.attend(q_lat[b, t], q_rope[b, t], c_kv[phys], k_rope[phys], w.scale)
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = the headline)")
+    ap.add_argument("--copies", type=int, default=4,
+                    help="input copies cycled through so repeats miss the 256 MB Infinity Cache")
+    ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic plan")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the verify call is a "
+              f"single-GPU kernel and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_decode_verify_mla_amd as mv
+    from speculative_decode_verify_mla_amd import synth
+    from speculative_decode_verify_mla_amd.synth import DL, DR
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mv.load_library()
+    dev = torch.device("cuda:0")
+    log(f"device {torch.cuda.get_device_name(0)}; workload config {args.config}")
+
+    w = synth.config(args.config)
+    wm = work_model(w)
+    log(f"workload {w.spec.name}: B={w.B} T={w.T} H={w.H} kv_lens={w.kv_lens.tolist()[:8]} "
+        f"algorithmic bytes {wm['total_bytes']/1e6:.2f} MB flops {wm['flops']:.4e}")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    # ---- device inputs, several copies -------------------------------------------
+    base = {}
+    base["q_lat"], base["q_rope"] = up(w.q_lat), up(w.q_rope)
+    if w.row_ids is None:
+        base["c_kv"], base["k_rope"] = up(w.c_kv), up(w.k_rope)
+    else:
+        base["c_kv"] = torch.full((w.kv_rows, DL), 0x7FC0, dtype=torch.int16, device=dev)
+        base["k_rope"] = torch.full((w.kv_rows, DR), 0x7FC0, dtype=torch.int16, device=dev)
+        rows = torch.from_numpy(w.row_ids).to(dev)
+        base["c_kv"][rows] = up(w.c_kv)
+        base["k_rope"][rows] = up(w.k_rope)
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(max(args.copies, 1) - 1)]
+    kv_lens = torch.from_numpy(w.kv_lens).to(dev)
+    mask = None if w.mask_for_kernel is None else torch.from_numpy(w.tree_mask).to(dev)
+    pt = None if w.page_table is None else torch.from_numpy(w.page_table).to(dev)
+    idx = None if w.indices is None else torch.from_numpy(w.indices).to(dev)
+    out = torch.empty((w.B, w.T, w.H, DL), dtype=torch.int16, device=dev)
+    lse = torch.empty((w.B, w.T, w.H), dtype=torch.float32, device=dev)
+    kw = dict(max_kv_len=w.max_kv_len, kv_seq_stride=w.kv_seq_stride, page_size=w.page_size,
+              num_splits=args.splits)
+    dims = mv.binding._dims_from(base["q_lat"], base["c_kv"], kv_lens, page_table=pt,
+                                 topk=0 if idx is None else idx.shape[2], phase=0, **kw)
+    info = mv.plan(dims, sparse=w.layout == "sparse")
+    ws = torch.empty(max(int(info.workspace_bytes), 16), dtype=torch.uint8, device=dev)
+    log(f"plan: splits={info.num_splits} chunk_tiles={info.chunk_tiles} row_blocks={info.row_blocks} "
+        f"groups={info.num_groups} workgroups={info.num_splits*info.row_blocks*info.num_groups} "
+        f"workspace={info.workspace_bytes/1e6:.1f} MB; inputs x{len(copies)} copies")
+    stream = torch.cuda.current_stream(dev)
+
+    def call(c, phase=mv.binding.PHASE_ALL):
+        if w.layout == "sparse":
+            mv.sparse_attn(c["q_lat"], c["q_rope"], c["c_kv"], c["k_rope"], pt, idx, kv_lens,
+                           w.scale, out, lse, workspace=ws, stream=stream, phase=phase, **kw)
+        else:
+            mv.verify_attn(c["q_lat"], c["q_rope"], c["c_kv"], c["k_rope"], pt, mask, kv_lens,
+                           w.scale, out, lse, workspace=ws, stream=stream, phase=phase, **kw)
+
+    # ---- warmup -----------------------------------------------------------------------
+    for i in range(args.warmup):
+        call(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} calls)")
+
+    # ---- timed region: K whole calls, inputs cycled across copies -------------------------
+    K = args.steps
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        call(copies[i % len(copies)])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / K
+    log(f"timed {K} calls: {ms_per_step*1e3:.2f} us/call (cold-rotated)")
+
+    # ---- warm (one copy, Infinity-Cache resident) for context ----------------------------
+    t_start.record(stream)
+    for i in range(K):
+        call(copies[0])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    warm_us = t_start.elapsed_time(t_end) / K * 1e3
+
+    # ---- per-kernel durations: HIP events around each phase on the launch stream ------------
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        c = copies[i % len(copies)]
+        ev[i][0].record(stream)
+        call(c, mv.binding.PHASE_PARTIAL)
+        ev[i][1].record(stream)
+        call(c, mv.binding.PHASE_COMBINE)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    combine_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    log(f"split kernel {split_ms*1e3:.2f} us, combine {combine_ms*1e3:.2f} us (event-timed)")
+
+    # ---- roofline of the dominant (split) kernel ------------------------------------------
+    t_hbm = wm["total_bytes"] / (PEAK_HBM_GBPS * 1e9)
+    t_mfma = wm["flops"] / (PEAK_BF16_TFLOPS * 1e12)
+    split_s = split_ms * 1e-3
+    if t_mfma >= t_hbm:
+        achieved = wm["flops"] / split_s / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4))
+    else:
+        split_bytes = wm["kv_bytes"] + wm["q_bytes"] + wm["meta_bytes"]
+        achieved = split_bytes / split_s / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
+                    unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4))
+    roof["traffic"] = load_traffic(w.spec.name)
+    roof["kernel"] = "mla_split_kernel"
+
+    value_us = ms_per_step * 1e3
+    gbps = wm["total_bytes"] / (value_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the fp64 oracle on the host for ~{args.cpu_budget:.0f} s")
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value_us, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, random draft tree)",
+        "config": {"workload": w.spec.name, "batch": w.B, "draft_tokens": w.T, "heads": w.H,
+                   "prefix": (w.kv_lens - w.T).tolist() if w.layout != "sparse" else None,
+                   "kv_lens": w.kv_lens.tolist()[:8] if w.B <= 8 else f"{w.B} x {int(w.kv_lens[0])}",
+                   "latent_dim": 512, "rope_dim": 64, "layout": w.layout,
+                   "topk": w.topk or None, "splits": int(info.num_splits),
+                   "workgroups": int(info.num_splits * info.row_blocks * info.num_groups)},
+        "achieved_hbm_GBps": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        "warm_us_per_call": round(warm_us, 3),
+        "split_kernel_us": round(split_ms * 1e3, 3),
+        "combine_kernel_us": round(combine_ms * 1e3, 3),
+        "algorithmic_bytes": int(wm["total_bytes"]),
+        "algorithmic_flops": wm["flops"],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernel_source": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def load_traffic(workload: str):
+    """HBM traffic per split-kernel launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            d = json.load(f)
+        if d.get("kernel_source") != kernel_source_hash():
+            return None
+        return d.get("traffic_bytes")
+    except Exception:
+        return None
+
+
+if __name__ == "__main__":
+    main()

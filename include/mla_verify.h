@@ -1,0 +1,165 @@
+/*
+ * mla_verify.h — C ABI of the MI355X (gfx950) MLA tree-verify attention library.
+ *
+ * Operation (both entry points): absorbed Multi-head Latent Attention for the
+ * draft tokens of a speculative-decoding tree. Every head of every draft token
+ * attends to one latent cache shared by all heads — a 512-wide latent row
+ * (c_kv) plus a 64-wide rotary row (k_rope) per cached token — under a
+ * prefix-plus-tree-ancestor mask, with a streaming (online) softmax that never
+ * materialises a score row.
+ *   - "The Shared Memory Ceiling", section "The Broader Context: Building a
+ *     Custom sm_120 Verify Kernel": verify attention inside DFlash/DDTree
+ *     speculative decoding; the MLA latent read once per head-tile instead of
+ *     once per head.
+ *   - same page, section "The Guard: Turning a Limitation into a
+ *     Demonstration": the Dl (latent) and Dr (rope) widths.
+ *   - same page, section "Technical Deep Dive: Why Shared Memory Matters":
+ *     score every visible key, normalise, take the weighted sum of the
+ *     512-dimensional values; online softmax keeps a running max and sum and
+ *     rescales earlier accumulations when the max grows.
+ *   - "The SMEM Ceiling", section "The Problem Space: Sparse Decode on
+ *     Blackwell": the sparse variant, where each token attends only to a top-k
+ *     index set, computed by a split kernel.
+ *
+ * For sequence b, draft token t, head h (row r = t*H + h):
+ *     s_p  = scale * (q_lat[b,t,h,:] . c_kv[row(p),:] + q_rope[b,t,h,:] . k_rope[row(p),:])
+ *     lse  = ln sum_{p in V} exp(s_p)                           (natural log, fp32)
+ *     out  = sum_{p in V} exp(s_p - lse) * c_kv[row(p),:]       (bf16, round-to-nearest-even)
+ * The values are the latent rows themselves: out stays in the 512-wide latent
+ * space (the per-head up-projection is outside this library), and k_rope is
+ * used only in the scores. RoPE is not applied here: q_rope and k_rope arrive
+ * already rotated. An empty visible set yields out = 0 and lse = -inf.
+ *
+ * Visible set V:
+ *   dense  (mla_verify_attn): the prefix positions p < kv_lens[b] - T, and
+ *          draft position kv_lens[b] - T + j whenever tree_mask[b,t,j] != 0
+ *          (a NULL tree_mask means a chain: j <= t). The T draft keys are the
+ *          last T positions of each sequence.
+ *   sparse (mla_sparse_attn): the positions indices[b,t,0..topk), shared by
+ *          all heads of token (b,t). Entries outside [0, kv_lens[b]) select
+ *          nothing (so -1 pads a short index list).
+ *
+ * Physical row of logical position p of sequence b:
+ *   contiguous (page_size == 0, page_table == NULL): b * kv_seq_stride + p
+ *   paged      (page_size  > 0, page_table != NULL):
+ *              page_table[b * max_pages + p / page_size] * page_size + p % page_size
+ *
+ * Layouts (all row-major, all device memory, all caller-owned):
+ *   q_lat   bf16 [B, T, H, 512]        q_rope  bf16 [B, T, H, 64]
+ *   c_kv    bf16 [kv_rows, 512]        k_rope  bf16 [kv_rows, 64]
+ *   out     bf16 [B, T, H, 512]        lse     fp32 [B, T, H]
+ *   kv_lens i32  [B]                   tree_mask u8 [B, T, T] or NULL
+ *   page_table i32 [B, max_pages] or NULL   indices i32 [B, T, topk]
+ *   bf16 is passed as its 16-bit pattern (uint16_t).
+ *
+ * Ownership and execution: the library never allocates, frees or
+ * synchronises, and never reads device data on the host. Work is enqueued
+ * on `stream` (a hipStream_t; NULL = the default stream) and returns
+ * immediately; inputs must stay alive until the stream work completes. Calls
+ * keep no state between them (a per-device capability check is cached) and
+ * may be captured into a HIP graph. Split-KV calls need a caller-provided
+ * device workspace of mla_verify_plan(...).workspace_bytes bytes; two calls in
+ * flight at once must not share one workspace.
+ *
+ * Errors: every function returns 0 on success or a negative MLA_ERR_* code.
+ * All argument checks run before any HIP call. Outputs are unspecified after
+ * an error. kv_lens[b] values are clamped to [0, max_kv_len] on the device;
+ * page_table entries that point outside [0, kv_rows) read as absent keys.
+ * No C++ exception crosses this boundary.
+ */
+#ifndef MLA_VERIFY_H
+#define MLA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_OK 0
+#define MLA_ERR_INVALID (-1)     /* bad argument: see the checks listed below */
+#define MLA_ERR_WORKSPACE (-2)   /* workspace NULL or smaller than the plan's workspace_bytes */
+#define MLA_ERR_HIP (-3)         /* a HIP runtime call or kernel launch failed */
+#define MLA_ERR_UNSUPPORTED (-4) /* the current device is not gfx950 */
+
+#define MLA_LATENT_DIM 512
+#define MLA_ROPE_DIM 64
+#define MLA_MAX_DRAFT 64  /* T limit: one 64-bit visibility word per query row */
+#define MLA_KV_TILE 64    /* keys per LDS tile; page_size must be a multiple */
+
+/* Which kernels a call enqueues. PARTIAL runs only the split-KV kernel (it
+ * writes the per-split partial results into the workspace, or the final
+ * out/lse when the plan has one split); COMBINE runs only the log-sum-exp
+ * merge of those partials into out/lse. ALL runs both. A PARTIAL call
+ * followed by a COMBINE call with identical arguments equals one ALL call. */
+#define MLA_PHASE_ALL 0
+#define MLA_PHASE_PARTIAL 1
+#define MLA_PHASE_COMBINE 2
+
+typedef struct mla_dims {
+  int32_t batch;         /* B >= 1 */
+  int32_t num_q;         /* T, 1..64 draft (query) tokens per sequence */
+  int32_t num_heads;     /* H >= 1 */
+  int32_t page_size;     /* 0 = contiguous cache; else tokens per page (multiple of 64) */
+  int32_t max_pages;     /* paged: entries per sequence in page_table */
+  int32_t max_kv_len;    /* host-known upper bound on kv_lens[]; plans the grid */
+  int64_t kv_seq_stride; /* contiguous: rows between consecutive sequences */
+  int64_t kv_rows;       /* rows of the c_kv and k_rope allocations */
+  int32_t topk;          /* sparse: index-list length per token (ignored by the dense call) */
+  int32_t num_splits;    /* 0 = automatic; else requested KV splits per query group */
+  int32_t phase;         /* MLA_PHASE_* */
+  int32_t reserved;      /* must be 0 */
+} mla_dims;
+
+typedef struct mla_plan_info {
+  int32_t num_splits;     /* KV splits per query group actually used */
+  int32_t chunk_tiles;    /* 64-key tiles per split */
+  int32_t row_blocks;     /* 128-row blocks per query group */
+  int32_t num_groups;     /* query groups: B (dense) or B*T (sparse) */
+  int32_t rows_per_group; /* T*H (dense) or H (sparse) */
+  int32_t reserved;
+  size_t workspace_bytes; /* device bytes the call needs; 0 when num_splits == 1 */
+} mla_plan_info;
+
+/* Work decomposition of a call with these dims (sparse != 0: mla_sparse_attn).
+ * Pure host arithmetic plus a one-time device-attribute query; no device
+ * memory is touched. Returns MLA_ERR_INVALID for dims the call would reject. */
+int mla_verify_plan(const mla_dims* dims, int sparse, mla_plan_info* plan);
+
+/* Convenience: mla_verify_plan(...).workspace_bytes, or 0 on invalid dims. */
+size_t mla_verify_workspace_bytes(const mla_dims* dims, int sparse);
+
+/* Dense tree-verify attention (see the file comment for the operation).
+ * Checks (MLA_ERR_INVALID): dims, q_lat, q_rope, c_kv, k_rope, kv_lens, out,
+ * lse non-NULL; bf16 arrays 16-byte aligned, lse/kv_lens/page_table 4-byte
+ * aligned; B >= 1, 1 <= T <= 64, H >= 1; T <= max_kv_len; num_splits >= 0;
+ * phase valid; reserved == 0; contiguous: page_table NULL, page_size 0,
+ * kv_seq_stride >= max_kv_len and (B-1)*kv_seq_stride + max_kv_len <= kv_rows;
+ * paged: page_table non-NULL, page_size a positive multiple of 64,
+ * max_pages * page_size >= max_kv_len. */
+int mla_verify_attn(const mla_dims* dims, const uint16_t* q_lat, const uint16_t* q_rope,
+                    const uint16_t* c_kv, const uint16_t* k_rope, const int32_t* page_table,
+                    const uint8_t* tree_mask, const int32_t* kv_lens, float scale,
+                    uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Sparse top-k attention: token (b,t) sees indices[b,t,0..topk) (logical
+ * positions of sequence b), shared by its H heads; no tree mask. Same checks
+ * as mla_verify_attn (minus the tree mask), plus: indices non-NULL and 4-byte
+ * aligned, topk >= 1; contiguous: kv_seq_stride <= 2^21 rows; paged:
+ * kv_rows <= 2^21 (the gather addresses rows with 32-bit byte offsets). */
+int mla_sparse_attn(const mla_dims* dims, const uint16_t* q_lat, const uint16_t* q_rope,
+                    const uint16_t* c_kv, const uint16_t* k_rope, const int32_t* page_table,
+                    const int32_t* indices, const int32_t* kv_lens, float scale,
+                    uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Static description of an error code (never NULL). */
+const char* mla_verify_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_VERIFY_H */

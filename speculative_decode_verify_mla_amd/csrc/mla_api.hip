@@ -1,0 +1,239 @@
+// Host side of libmla_verify: argument checks, work decomposition (split
+// plan), workspace sizing and kernel dispatch behind the C ABI of
+// include/mla_verify.h. Every check runs before the first HIP call; no call
+// allocates, frees, synchronises or reads device memory on the host.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "mla_internal.h"
+#include "mla_verify.h"
+
+namespace {
+
+using mlav::kRowsPerBlock;
+using mlav::kTile;
+using mlav::kWaves;
+
+constexpr int kMaxDevices = 64;
+// Per-device cache: 0 = unknown, 1 = gfx950, -1 = other. CU count alongside.
+std::atomic<int> g_arch_state[kMaxDevices];
+std::atomic<int> g_cu_count[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Host-side shape checks shared by both entry points. Returns MLA_OK or MLA_ERR_INVALID.
+int check_dims(const mla_dims* d, bool sparse, bool paged) {
+  if (d == nullptr) return MLA_ERR_INVALID;
+  if (d->batch < 1 || d->num_q < 1 || d->num_q > MLA_MAX_DRAFT || d->num_heads < 1)
+    return MLA_ERR_INVALID;
+  if (d->num_splits < 0 || d->reserved != 0) return MLA_ERR_INVALID;
+  if (d->phase < MLA_PHASE_ALL || d->phase > MLA_PHASE_COMBINE) return MLA_ERR_INVALID;
+  if (d->max_kv_len < 1 || d->kv_rows < 1) return MLA_ERR_INVALID;
+  if (!sparse && d->max_kv_len < d->num_q) return MLA_ERR_INVALID;
+  if (sparse && d->topk < 1) return MLA_ERR_INVALID;
+  // row counts must fit 32-bit grid arithmetic
+  const int64_t rows_total = (int64_t)d->batch * d->num_q * d->num_heads;
+  if (rows_total > (int64_t)1 << 30) return MLA_ERR_INVALID;
+  if (paged) {
+    if (d->page_size <= 0 || d->page_size % kTile != 0) return MLA_ERR_INVALID;
+    if (d->max_pages < 1) return MLA_ERR_INVALID;
+    if ((int64_t)d->max_pages * d->page_size < d->max_kv_len) return MLA_ERR_INVALID;
+    if (sparse && d->kv_rows > ((int64_t)1 << 21)) return MLA_ERR_INVALID;
+  } else {
+    if (d->kv_seq_stride < d->max_kv_len) return MLA_ERR_INVALID;
+    if ((int64_t)(d->batch - 1) * d->kv_seq_stride + d->max_kv_len > d->kv_rows)
+      return MLA_ERR_INVALID;
+    if (sparse && d->kv_seq_stride > ((int64_t)1 << 21)) return MLA_ERR_INVALID;
+  }
+  return MLA_OK;
+}
+
+// CU count of the current device (256 when it cannot be queried: planning only).
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int c = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 256;
+  g_cu_count[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// MLA_OK on gfx950, MLA_ERR_UNSUPPORTED elsewhere, MLA_ERR_HIP if the runtime fails.
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_HIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MLA_OK : MLA_ERR_UNSUPPORTED;
+}
+
+int make_plan(const mla_dims* d, bool sparse, mla_plan_info* p) {
+  const int64_t groups = sparse ? (int64_t)d->batch * d->num_q : d->batch;
+  const int64_t rows = sparse ? d->num_heads : (int64_t)d->num_q * d->num_heads;
+  const int64_t row_blocks = ceil_div(rows, kRowsPerBlock);
+  const int64_t keys = sparse ? d->topk : d->max_kv_len;
+  const int64_t tiles = ceil_div(keys, kTile);
+  int64_t splits;
+  if (d->num_splits > 0) {
+    splits = d->num_splits;
+  } else {
+    // One workgroup per CU (LDS-bound): spread the keys of each query group
+    // over enough splits to cover the CUs once, but keep >= 4 tiles per split
+    // so the per-split partial (2 KB per row) stays small next to its KV reads.
+    const int64_t per_split = groups * row_blocks;
+    splits = device_cus() / per_split;
+    const int64_t min_tiles_cap = tiles / 4;
+    if (splits > min_tiles_cap) splits = min_tiles_cap;
+    if (splits < 1) splits = 1;
+  }
+  if (splits > tiles) splits = tiles;
+  int64_t chunk = ceil_div(tiles, splits);
+  splits = ceil_div(tiles, chunk);
+  const int64_t grid = row_blocks * splits * groups;
+  if (grid > 0x7fffffff) return MLA_ERR_INVALID;
+  p->num_splits = (int32_t)splits;
+  p->chunk_tiles = (int32_t)chunk;
+  p->row_blocks = (int32_t)row_blocks;
+  p->num_groups = (int32_t)groups;
+  p->rows_per_group = (int32_t)rows;
+  p->reserved = 0;
+  p->workspace_bytes =
+      splits > 1 ? (size_t)splits * groups * row_blocks * kWaves * mlav::kRecBytes : 0;
+  return MLA_OK;
+}
+
+int run(const mla_dims* d, bool sparse, const uint16_t* q_lat, const uint16_t* q_rope,
+        const uint16_t* c_kv, const uint16_t* k_rope, const int32_t* page_table,
+        const uint8_t* tree_mask, const int32_t* indices, const int32_t* kv_lens, float scale,
+        uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (d == nullptr) return MLA_ERR_INVALID;
+  // a page table and a page size come together, or neither does
+  if ((page_table != nullptr) != (d->page_size != 0)) return MLA_ERR_INVALID;
+  int rc = check_dims(d, sparse, page_table != nullptr);
+  if (rc != MLA_OK) return rc;
+  if (!q_lat || !q_rope || !c_kv || !k_rope || !kv_lens || !out || !lse) return MLA_ERR_INVALID;
+  if (sparse && !indices) return MLA_ERR_INVALID;
+  if (!aligned(q_lat, 16) || !aligned(q_rope, 16) || !aligned(c_kv, 16) || !aligned(k_rope, 16) ||
+      !aligned(out, 16) || !aligned(lse, 4) || !aligned(kv_lens, 4))
+    return MLA_ERR_INVALID;
+  if ((page_table && !aligned(page_table, 4)) || (indices && !aligned(indices, 4)))
+    return MLA_ERR_INVALID;
+  if (!(scale == scale)) return MLA_ERR_INVALID;  // NaN scale
+  mla_plan_info p;
+  rc = make_plan(d, sparse, &p);
+  if (rc != MLA_OK) return rc;
+  if (p.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < p.workspace_bytes || !aligned(workspace, 16))
+      return MLA_ERR_WORKSPACE;
+  }
+  rc = check_device();
+  if (rc != MLA_OK) return rc;
+
+  mlav::MainArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q_lat = q_lat;
+  a.q_rope = q_rope;
+  a.c_kv = c_kv;
+  a.k_rope = k_rope;
+  a.page_table = page_table;
+  a.tree_mask = sparse ? nullptr : tree_mask;
+  a.kv_lens = kv_lens;
+  a.indices = sparse ? indices : nullptr;
+  a.out = out;
+  a.lse = lse;
+  if (p.workspace_bytes > 0) {
+    const size_t records = (size_t)p.num_splits * p.num_groups * p.row_blocks * kWaves;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_lse = a.ws_o + records * mlav::kRecFloats;
+  }
+  a.kv_seq_stride = page_table ? 0 : d->kv_seq_stride;
+  a.kv_rows = d->kv_rows;
+  a.T = d->num_q;
+  a.H = d->num_heads;
+  a.rows_per_group = p.rows_per_group;
+  a.num_groups = p.num_groups;
+  a.row_blocks = p.row_blocks;
+  a.page_size = page_table ? d->page_size : 0;
+  a.max_pages = page_table ? d->max_pages : 0;
+  a.max_kv_len = d->max_kv_len;
+  a.topk = sparse ? d->topk : 0;
+  a.num_splits = p.num_splits;
+  a.chunk_tiles = p.chunk_tiles;
+  a.final_out = p.num_splits == 1 ? 1 : 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  const int mode = sparse ? (page_table ? mlav::kSparsePaged : mlav::kSparse)
+                          : (page_table ? mlav::kPaged : mlav::kContig);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // With a single split the split kernel writes out/lse itself and there is
+  // nothing to combine.
+  if (d->phase != MLA_PHASE_COMBINE) {
+    if (mlav::launch_split_kernel(a, mode, s) != hipSuccess) return MLA_ERR_HIP;
+  }
+  if (!a.final_out && d->phase != MLA_PHASE_PARTIAL) {
+    if (mlav::launch_combine_kernel(a, mode, s) != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_verify_plan(const mla_dims* dims, int sparse, mla_plan_info* plan) {
+  if (plan == nullptr || dims == nullptr) return MLA_ERR_INVALID;
+  const int rc = check_dims(dims, sparse != 0, dims->page_size != 0);
+  if (rc != MLA_OK) return rc;
+  return make_plan(dims, sparse != 0, plan);
+}
+
+size_t mla_verify_workspace_bytes(const mla_dims* dims, int sparse) {
+  mla_plan_info p;
+  if (mla_verify_plan(dims, sparse, &p) != MLA_OK) return 0;
+  return p.workspace_bytes;
+}
+
+int mla_verify_attn(const mla_dims* dims, const uint16_t* q_lat, const uint16_t* q_rope,
+                    const uint16_t* c_kv, const uint16_t* k_rope, const int32_t* page_table,
+                    const uint8_t* tree_mask, const int32_t* kv_lens, float scale,
+                    uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return run(dims, false, q_lat, q_rope, c_kv, k_rope, page_table, tree_mask, nullptr, kv_lens,
+             scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_sparse_attn(const mla_dims* dims, const uint16_t* q_lat, const uint16_t* q_rope,
+                    const uint16_t* c_kv, const uint16_t* k_rope, const int32_t* page_table,
+                    const int32_t* indices, const int32_t* kv_lens, float scale,
+                    uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return run(dims, true, q_lat, q_rope, c_kv, k_rope, page_table, nullptr, indices, kv_lens,
+             scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+const char* mla_verify_strerror(int code) {
+  switch (code) {
+    case MLA_OK: return "success";
+    case MLA_ERR_INVALID: return "invalid argument";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime or launch failure";
+    case MLA_ERR_UNSUPPORTED: return "device is not gfx950";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

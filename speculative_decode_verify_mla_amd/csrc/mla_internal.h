@@ -1,0 +1,57 @@
+// Internal types shared by the host dispatcher and the kernels of libmla_verify.
+// Not part of the public ABI (that is include/mla_verify.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlav {
+
+constexpr int kDL = 512;             // latent width (values and the first score term)
+constexpr int kDR = 64;              // rotary width (second score term only)
+constexpr int kTile = 64;            // keys per LDS tile
+constexpr int kWaves = 4;            // waves per workgroup
+constexpr int kRowsPerWave = 32;     // query rows owned by one wave (one per lane pair)
+constexpr int kRowsPerBlock = kWaves * kRowsPerWave;  // 128
+constexpr int kThreads = kWaves * 64;
+
+// Workspace record: one wave's 32 rows x 512 fp32 partial output, plus 32 lse values.
+constexpr int kRecFloats = kRowsPerWave * kDL;  // 16384
+constexpr size_t kRecBytes = (size_t)kRecFloats * 4 + (size_t)kRowsPerWave * 4;
+
+enum Mode : int { kContig = 0, kPaged = 1, kSparse = 2, kSparsePaged = 3 };
+
+struct MainArgs {
+  const uint16_t* q_lat;
+  const uint16_t* q_rope;
+  const uint16_t* c_kv;
+  const uint16_t* k_rope;
+  const int32_t* page_table;
+  const uint8_t* tree_mask;
+  const int32_t* kv_lens;
+  const int32_t* indices;
+  uint16_t* out;
+  float* lse;
+  float* ws_o;    // [records][16384] fp32, register-native order
+  float* ws_lse;  // [records][32] fp32, log2 domain
+  int64_t kv_seq_stride;
+  int64_t kv_rows;
+  int32_t T, H;
+  int32_t rows_per_group;
+  int32_t num_groups;
+  int32_t row_blocks;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t max_kv_len;
+  int32_t topk;
+  int32_t num_splits;
+  int32_t chunk_tiles;
+  int32_t final_out;   // 1: single split, write out/lse directly
+  float scale_log2;    // scale * log2(e)
+};
+
+// Launchers (defined in mla_kernels.hip). Return the hipError_t of the launch.
+hipError_t launch_split_kernel(const MainArgs& a, int mode, hipStream_t stream);
+hipError_t launch_combine_kernel(const MainArgs& a, int mode, hipStream_t stream);
+
+}  // namespace mlav

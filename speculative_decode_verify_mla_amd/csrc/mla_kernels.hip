@@ -1,0 +1,647 @@
+// MLA tree-verify attention kernels for gfx950 (CDNA4).
+//
+// What is computed ("The Shared Memory Ceiling", sections "The Broader
+// Context" and "Technical Deep Dive: Why Shared Memory Matters"): every query
+// row (draft token t, head h) scores the visible keys of one latent cache
+// (512 latent + 64 rope dims, shared by all heads), and returns the
+// softmax-weighted sum of the 512-wide latent rows plus the log-sum-exp. The
+// score row is never stored: an online softmax keeps a running max and sum per
+// row and rescales the accumulator when the max grows. Long key ranges are
+// split across workgroups and merged by a log-sum-exp combine (the "split
+// kernel" of "The SMEM Ceiling", section "The Problem Space").
+//
+// Design on gfx950 (the pages' sm_120 head-tile of 8 heads is prior art):
+//  * A workgroup is 4 waves x 32 query rows = 128 rows that share every KV
+//    tile; 2 LDS stages of 64 keys (73,728 B each) fit the 160 KB LDS.
+//  * Tiles move HBM -> LDS with 16-byte buffer loads that write LDS directly
+//    (buffer_load_dwordx4 ... lds). Buffer range checks zero-fill keys past the
+//    end of a sequence, outside the index set, or on an invalid page, so masked
+//    value rows are 0 (never stale NaN) in the PV product.
+//  * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16 with the K tile as the LDS
+//    operand and Q held in registers. In the 32x32 accumulator layout each lane
+//    then owns one query row (16 keys per block, two lanes per row), so the row
+//    max is an in-lane max plus one exchange with lane^32, and the row sum stays
+//    per-lane until the end.
+//  * The same accumulator registers, rounded to bf16, are directly the B
+//    operand of O^T += V^T * P^T (the key order inside each 16-key step is
+//    permuted identically on both operands). V^T comes from the row-major tile
+//    through ds_read_b64_tr_b16 (transposing LDS read), so K and V share one
+//    tile (MLA's value rows are the first 512 dims of its key rows).
+//  * The 256 accumulator registers per lane are never rescaled in the loop (a
+//    VALU rescale would pull them out of the accumulation registers): exponents
+//    use a fixed per-row reference, with an exact two-pass fallback when a
+//    later score exceeds it by more than 2^32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mlav {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kLatBytes = kTile * kDL * 2;    // 65536: latent part of a tile
+constexpr int kRopeBytes = kTile * kDR * 2;   // 8192: rope part of a tile
+constexpr int kStageBytes = kLatBytes + kRopeBytes;  // 73728
+constexpr int kStages = 2;
+constexpr int kLdsBytes = kStages * kStageBytes;  // 147456
+static_assert(kLdsBytes + 16 <= 163840, "two KV stages must fit one gfx950 CU's 160 KB LDS");
+constexpr int kLoadsPerStage = kStageBytes / (64 * 16);  // 72 wave-wide 16-byte loads
+static_assert(kLoadsPerStage == 72 && kLoadsPerStage % kWaves == 0, "load split");
+constexpr unsigned kBufferConfig = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr unsigned kOobOffset = 0x80000000u;     // an offset every range check rejects
+constexpr float kOverflowLog2 = 32.0f;           // largest exponent (log2 units) a term may take
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// ---------------------------------------------------------------------------
+// LDS swizzles. A tile is stored row-major (key-major) with its 16-byte chunks
+// permuted inside each key row so that the two read patterns are free of bank
+// conflicts: 16 consecutive keys reading the same logical chunk (S^T operand),
+// and 4 consecutive keys x 32 bytes (transposing V^T read).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz_lat(int key) {  // permutes the low 4 chunk bits
+  return ((key & 3) << 1) | ((key >> 2) & 1) | (key & 8);
+}
+__device__ __forceinline__ int swz_rope(int key) {  // permutes the 3 chunk bits
+  return ((key >> 1) ^ (key << 2)) & 7;
+}
+
+// Generic -> LDS address-space pointers (the arrays live in LDS; the casts only
+// let the compiler emit ds_* / LDS-DMA instructions directly).
+__device__ __forceinline__ bf16x8 lds_read16(const uint8_t* base, unsigned off) {
+  const LDS_AS uint8_t* p = (const LDS_AS uint8_t*)(base) + off;
+  return *(const LDS_AS bf16x8*)p;
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* base, unsigned off) {
+  LDS_AS uint8_t* p = (LDS_AS uint8_t*)(base) + off;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
+}
+
+__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds_dst,
+                                              unsigned voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(lds_dst), 16, voffset, 0, 0, 0);
+}
+
+// Buffer descriptors are wave-uniform; readfirstlane keeps them in SGPRs even
+// when the compiler cannot prove uniformity (it would otherwise emit a loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           (int)kBufferConfig);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Score MFMAs with VGPR accumulators. Every accumulating MFMA in a function is
+// otherwise given AGPR accumulators, and the 256 output accumulators already
+// fill the AGPR file; scores are consumed by VALU code, so they belong in VGPRs.
+// The hardware resolves back-to-back accumulation into the same registers;
+// reading the result with VALU needs the wait states of score_fence().
+__device__ __forceinline__ f32x16 mfma32_v_first(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma32_v_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// Independent-instruction wait states between the last score MFMA and any
+// VALU/VMEM/LDS access of its result (more than a 16-pass XDL op requires).
+__device__ __forceinline__ void score_fence(f32x16& s0, f32x16& s1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Keys of one query group and how its tiles are split (shared by both kernels).
+struct GroupInfo {
+  int b;        // sequence
+  int kv_len;   // clamped kv_lens[b]
+  int n_tiles;  // 64-key tiles covering the group's key list
+};
+
+__device__ __forceinline__ GroupInfo group_info(const MainArgs& a, int group, bool sparse) {
+  GroupInfo g;
+  g.b = sparse ? group / a.T : group;
+  int kv = a.kv_lens[g.b];
+  kv = kv < 0 ? 0 : (kv > a.max_kv_len ? a.max_kv_len : kv);
+  g.kv_len = kv;
+  const int n_keys = sparse ? a.topk : kv;
+  g.n_tiles = (n_keys + kTile - 1) / kTile;
+  return g;
+}
+
+// ---------------------------------------------------------------------------
+// Split kernel: one workgroup = (row block, split, query group).
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_split_kernel(MainArgs a) {
+  constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
+  constexpr bool kPagedMode = MODE == kPaged || MODE == kSparsePaged;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes + 16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;  // which 16-key half of the 32x32 accumulator a lane holds
+  const int l32 = lane & 31;
+
+  const int sg = a.num_splits * a.num_groups;
+  const int bid = blockIdx.x;
+  const int rb = bid / sg;
+  const int rem = bid - rb * sg;
+  const int split = rem / a.num_groups;
+  const int group = rem - split * a.num_groups;
+
+  const GroupInfo gi = group_info(a, group, kSparseMode);
+  const int b = gi.b;
+  const int kv_len = gi.kv_len;
+  const int t_begin = split * a.chunk_tiles;
+  const int t_end = min(t_begin + a.chunk_tiles, gi.n_tiles);
+
+  const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave;
+  const bool wave_active = row0 < a.rows_per_group;
+  const int row = row0 + l32;
+  const bool row_valid = row < a.rows_per_group;
+  const int64_t qrow = (int64_t)group * a.rows_per_group + row;
+
+  if (t_begin >= t_end) {
+    // No keys for this group at all (only reachable with a single split): empty softmax.
+    if (a.final_out && split == 0 && row_valid) {
+      uint2 z = {0u, 0u};
+      for (int d = 4 * half; d < kDL; d += 8)
+        *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = z;
+      if (half == 0) a.lse[qrow] = -__builtin_inff();
+    }
+    return;
+  }
+
+  // ---- query rows into registers: the B operand of S^T = K Q^T ------------
+  // Lane (row l32, half h) holds dims 16c + 8h .. +7 of chunk c (c < 32: latent).
+  // Padding rows (past the group's rows) load row 0 of the group and are zeroed.
+  bf16x8 q[36];
+  {
+    const int64_t qsrc = row_valid ? qrow : (int64_t)group * a.rows_per_group;
+#pragma unroll
+    for (int c = 0; c < 36; ++c) {
+      const uint16_t* src = c < 32 ? a.q_lat + qsrc * kDL + 16 * c + 8 * half
+                                   : a.q_rope + qsrc * kDR + 16 * (c - 32) + 8 * half;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(src);
+      q[c] = row_valid ? v : bf16x8{};
+    }
+  }
+
+  // ---- visibility of the T draft keys for this lane's row (dense) ----------
+  uint64_t vis = 0;
+  const int prefix = kv_len - a.T;
+  if (!kSparseMode && row_valid) {
+    const int t = row / a.H;
+    if (a.tree_mask != nullptr) {
+      const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.T + t) * a.T;
+      for (int j = 0; j < a.T; ++j)
+        if (mrow[j] != 0) vis |= 1ull << j;
+    } else {
+      vis = (t >= 63) ? ~0ull : ((2ull << t) - 1ull);  // chain: drafts 0..t
+    }
+  }
+
+  // ---- per-lane LDS read offsets ------------------------------------------
+  // S^T operand: key = kb*32 + l32, logical chunk 2c + half; the XOR swizzle
+  // acts on the low 4 chunk bits, so 8 offsets cover the 32 latent chunks and
+  // (c >> 3) * 256 is an immediate.
+  const int xlat = half ^ swz_lat(l32);
+  const int yrope = half ^ swz_rope(l32);
+  unsigned offA[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) offA[j] = l32 * 1024 + (((2 * j) ^ xlat) * 16);
+  // V^T operand through the transposing read: within each 16-lane group G,
+  // lane i addresses key (base + i/4) and 4 dims starting at 4*(i%4); the
+  // hardware hands lane i the 4 keys of dim i. Two reads cover 8 keys.
+  unsigned offV[2][4];
+  {
+    const int G = lane >> 4, i = lane & 15, h = lane >> 5;
+    const int u = 2 * (G & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int second = 0; second < 2; ++second) {
+      const int key = 8 * second + 4 * h + (i >> 2);
+      const int sw = swz_lat(key);
+#pragma unroll
+      for (int dq = 0; dq < 4; ++dq)
+        offV[second][dq] = key * 1024 + ((((4 * dq) | u) ^ sw) * 16) + 8 * (i & 1);
+    }
+  }
+
+  // ---- tile loads ------------------------------------------------------------
+  // Wave w issues loads w + 4*i: i < 16 -> one latent key row (key w + 4i, lane =
+  // stored chunk), i = 16, 17 -> rope rows of keys 8j .. 8j+7 with j = w, w + 4.
+  // Byte offset, within a key row, of the logical chunk stored at slot `lane`:
+  auto lat_chunk_off = [&](int key) -> unsigned { return (unsigned)((lane ^ swz_lat(key & 15)) * 16); };
+  const unsigned rope_chunk_off =
+      (unsigned)(((lane & 7) ^ swz_rope(8 * wave + (lane >> 3))) * 16);  // same for j = w + 4
+
+  const int64_t seq_row0 = kPagedMode ? 0 : (int64_t)b * a.kv_seq_stride;
+
+  // Sparse: lane k holds the physical row of key k of a tile (-1 = absent).
+  auto fetch_index = [&](int tile) -> int {
+    const int k = tile * kTile + lane;
+    return k < a.topk ? a.indices[(int64_t)group * a.topk + k] : -1;
+  };
+  auto resolve_row = [&](int idx) -> int {
+    if (idx < 0 || idx >= kv_len) return -1;
+    if (!kPagedMode) return idx;
+    const int page = a.page_table[(int64_t)b * a.max_pages + idx / a.page_size];
+    if (page < 0) return -1;
+    const int64_t r = (int64_t)page * a.page_size + idx % a.page_size;
+    return r < a.kv_rows ? (int)r : -1;
+  };
+
+  // Dense: issue one tile; returns the number of leading keys that exist.
+  auto issue_dense = [&](int tile, int stage) -> int {
+    uint8_t* dst = smem + stage * kStageBytes;
+    const int pos = tile * kTile;
+    int nv = min(kTile, kv_len - pos);
+    int64_t rbase;
+    if (kPagedMode) {
+      const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
+      rbase = (int64_t)page * a.page_size + pos % a.page_size;
+      if (page < 0 || rbase >= a.kv_rows) {
+        nv = 0;
+        rbase = 0;
+      } else if (rbase + nv > a.kv_rows) {
+        nv = (int)(a.kv_rows - rbase);
+      }
+    } else {
+      rbase = seq_row0 + pos;
+    }
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.c_kv + rbase * kDL, (uint32_t)nv * 1024u);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.k_rope + rbase * kDR, (uint32_t)nv * 128u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = wave + 4 * i;
+      buffer_to_lds(rl, dst + key * 1024, (unsigned)key * 1024u + lat_chunk_off(key));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = wave + 4 * i;
+      buffer_to_lds(rr, dst + kLatBytes + j * 1024,
+                    (unsigned)j * 1024u + (unsigned)((lane >> 3) * 128) + rope_chunk_off);
+    }
+    return nv;
+  };
+
+  // Sparse: issue one tile given lane k's physical row for key k.
+  // (the host limits sparse extents to 2^21 rows, so byte offsets stay below 2^31)
+  const int64_t sparse_rows = kPagedMode ? a.kv_rows : (int64_t)kv_len;
+  auto issue_sparse = [&](int rows, int stage) {
+    uint8_t* dst = smem + stage * kStageBytes;
+    const __amdgpu_buffer_rsrc_t srl =
+        make_rsrc(a.c_kv + seq_row0 * kDL, (uint32_t)(sparse_rows * 1024));
+    const __amdgpu_buffer_rsrc_t srr =
+        make_rsrc(a.k_rope + seq_row0 * kDR, (uint32_t)(sparse_rows * 128));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = wave + 4 * i;
+      const int r = __builtin_amdgcn_readlane(rows, key);
+      const unsigned off = r >= 0 ? (unsigned)r * 1024u + lat_chunk_off(key) : kOobOffset;
+      buffer_to_lds(srl, dst + key * 1024, off);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = wave + 4 * i;
+      const int r = __shfl(rows, 8 * j + (lane >> 3));
+      const unsigned off = r >= 0 ? (unsigned)r * 128u + rope_chunk_off : kOobOffset;
+      buffer_to_lds(srr, dst + kLatBytes + j * 1024, off);
+    }
+  };
+
+  // ---- softmax state ------------------------------------------------------------
+  // The accumulator is never rescaled inside the loop: every exponent is taken
+  // against a fixed per-row reference m_ref (the row max of the first tile with
+  // a visible key). If a later score exceeds m_ref by more than 2^32 (log2
+  // units), the split is run a second time with m_ref = the true row max, so
+  // no exponent ever exceeds 2^32 and the result is exact either way.
+  f32x16 o[16];
+  float m_ref = -__builtin_inff();   // log2 domain; equal in both lanes of a row
+  float m_true = -__builtin_inff();  // this lane's max over every visible score
+  float l_run = 0.f;                 // this lane's share of the row sum (fp32 terms: the lse)
+  float lq_run = 0.f;                // the same sum over the bf16-rounded terms fed to PV
+  int* restart_flag = reinterpret_cast<int*>(smem + kLdsBytes);
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) o[d] = f32x16{};
+    l_run = 0.f;
+    lq_run = 0.f;
+    bool overflow = false;
+
+    // ---- prologue --------------------------------------------------------------
+    int nv_cur = 0, nv_next = 0;
+    uint64_t vm_cur = 0, vm_next = 0;
+    int idx_next = -1;
+    if (kSparseMode) {
+      const int r0 = resolve_row(fetch_index(t_begin));
+      vm_cur = __ballot(r0 >= 0);
+      issue_sparse(r0, 0);
+      if (t_begin + 1 < t_end) idx_next = fetch_index(t_begin + 1);
+    } else {
+      nv_cur = issue_dense(t_begin, 0);
+    }
+    if (threadIdx.x == 0) *restart_flag = 0;
+
+    for (int tile = t_begin; tile < t_end; ++tile) {
+      const int stage = (tile - t_begin) & 1;
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads (tile data, prefetched indices) landed
+      __syncthreads();                // ... and every other wave's; previous stage is free
+      if (tile + 1 < t_end) {
+        if (kSparseMode) {
+          const int r1 = resolve_row(idx_next);
+          vm_next = __ballot(r1 >= 0);
+          issue_sparse(r1, stage ^ 1);
+          if (tile + 2 < t_end) idx_next = fetch_index(tile + 2);
+        } else {
+          nv_next = issue_dense(tile + 1, stage ^ 1);
+        }
+      }
+
+      if (wave_active) {
+        const uint8_t* sb = smem + stage * kStageBytes;
+        // -- S^T = K Q^T over 576 dims: two 32-key blocks ------------------------
+        // K fragments are read one 16-dim step ahead of the MFMAs that use them.
+        auto k_off = [&](int c) -> unsigned {
+          return c < 32 ? offA[c & 7] + (unsigned)((c >> 3) * 256)
+                        : (unsigned)(kLatBytes + l32 * 128 + (((2 * (c - 32)) ^ yrope) * 16));
+        };
+        auto k_blk = [&](int c) -> unsigned { return c < 32 ? 32u * 1024u : 32u * 128u; };
+        f32x16 s0, s1;
+        bf16x8 ka0 = lds_read16(sb, k_off(0));
+        bf16x8 ka1 = lds_read16(sb, k_off(0) + k_blk(0));
+#pragma unroll
+        for (int c = 0; c < 36; ++c) {
+          bf16x8 kb0 = ka0, kb1 = ka1;
+          if (c + 1 < 36) {
+            kb0 = lds_read16(sb, k_off(c + 1));
+            kb1 = lds_read16(sb, k_off(c + 1) + k_blk(c + 1));
+          }
+          if (c == 0) {
+            s0 = mfma32_v_first(ka0, q[c]);
+            s1 = mfma32_v_first(ka1, q[c]);
+          } else {
+            mfma32_v_acc(s0, ka0, q[c]);
+            mfma32_v_acc(s1, ka1, q[c]);
+          }
+          ka0 = kb0;
+          ka1 = kb1;
+        }
+        score_fence(s0, s1);
+
+        // -- scale into log2 units and mask ---------------------------------------
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[r] *= a.scale_log2;
+          s1[r] *= a.scale_log2;
+        }
+        const int pos0 = tile * kTile;
+        const bool need_mask = kSparseMode ? (vm_cur != ~0ull)
+                                           : (nv_cur < kTile || pos0 + kTile > prefix);
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 32; ++r) {
+            // accumulator register r%16 of block r/16 holds key 8*((r%16)/4) + 4*half + r%4
+            const int key = 32 * (r >> 4) + 8 * ((r & 15) >> 2) + 4 * half + (r & 3);
+            bool ok;
+            if (kSparseMode) {
+              ok = (vm_cur >> key) & 1ull;
+            } else {
+              const int p = pos0 + key;
+              ok = key < nv_cur && (p < prefix || ((vis >> ((p - prefix) & 63)) & 1ull));
+            }
+            if (r < 16) s0[r] = ok ? s0[r] : -__builtin_inff();
+            else s1[r - 16] = ok ? s1[r - 16] : -__builtin_inff();
+          }
+        }
+
+        // -- reference max and overflow check --------------------------------------
+        float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+        m_true = fmaxf(m_true, mx);
+        if (__ballot(m_ref == -__builtin_inff() && mx != -__builtin_inff()) != 0ull) {
+          // first visible keys of some row: its reference is this tile's row max
+          // (its accumulator and sum are still zero, so nothing is rescaled)
+          const float row_mx = fmaxf(mx, __shfl_xor(mx, 32));
+          m_ref = m_ref == -__builtin_inff() ? row_mx : m_ref;
+        }
+        overflow = overflow || (mx > m_ref + kOverflowLog2);
+        const float m_use = m_ref == -__builtin_inff() ? 0.f : m_ref;
+
+        // -- P = 2^(s - m_ref), row sums, bf16 operand for the PV product -------------
+        // The output is normalised by the sum of the rounded terms it actually
+        // accumulated (an exact convex combination of value rows); the lse uses
+        // the fp32 terms.
+        float psum = 0.f, qsum = 0.f;
+        bf16x8 pk[4];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p0 = fast_exp2(fminf(s0[r] - m_use, kOverflowLog2));
+          const float p1 = fast_exp2(fminf(s1[r] - m_use, kOverflowLog2));
+          const __bf16 b0 = (__bf16)p0, b1 = (__bf16)p1;
+          psum += p0 + p1;
+          qsum += (float)b0 + (float)b1;
+          pk[r >> 3][r & 7] = b0;
+          pk[2 + (r >> 3)][r & 7] = b1;
+        }
+        l_run += psum;
+        lq_run += qsum;
+
+        // -- O^T += V^T P^T: 16 blocks of 32 dims x 4 steps of 16 keys -------------
+        // V^T fragments are read one step ahead of the MFMA that uses them.
+        auto v_frag = [&](int step) -> bf16x8 {
+          const int db = step >> 2, kc = step & 3;
+          const unsigned hi = (unsigned)((db >> 2) * 256 + kc * 16384);
+          const bf16x4 v0 = lds_read_tr(sb, offV[0][db & 3] + hi);
+          const bf16x4 v1 = lds_read_tr(sb, offV[1][db & 3] + hi);
+          return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        };
+        bf16x8 va = v_frag(0);
+#pragma unroll
+        for (int step = 0; step < 64; ++step) {
+          bf16x8 vb = va;
+          if (step + 1 < 64) vb = v_frag(step + 1);
+          o[step >> 2] = mfma32(va, pk[step & 3], o[step >> 2]);
+          va = vb;
+        }
+      }
+      nv_cur = nv_next;
+      vm_cur = vm_next;
+    }
+
+    // Run the split again only if some row of the workgroup overflowed.
+    if (overflow) *restart_flag = 1;
+    __syncthreads();
+    const bool again = pass == 0 && *restart_flag != 0;
+    __syncthreads();
+    if (!again) break;
+    const float row_true = fmaxf(m_true, __shfl_xor(m_true, 32));
+    m_ref = row_true;
+  }
+
+  if (!wave_active) return;
+
+  // ---- epilogue ------------------------------------------------------------------
+  const float l_row = l_run + __shfl_xor(l_run, 32);
+  const float lq_row = lq_run + __shfl_xor(lq_run, 32);
+  const bool live = l_row > 0.f;
+  const float inv = live && lq_row > 0.f ? 1.0f / lq_row : 0.f;
+  const float lse2 = live ? m_ref + fast_log2(l_row) : -__builtin_inff();
+  if (a.final_out) {
+    if (row_valid) {
+      uint16_t* dst = a.out + qrow * kDL;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int d = db * 32 + 8 * qq + 4 * half;
+          uint2 pkd;
+          pkd.x = (uint32_t)bf16_bits(o[db][4 * qq + 0] * inv) |
+                  ((uint32_t)bf16_bits(o[db][4 * qq + 1] * inv) << 16);
+          pkd.y = (uint32_t)bf16_bits(o[db][4 * qq + 2] * inv) |
+                  ((uint32_t)bf16_bits(o[db][4 * qq + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(dst + d) = pkd;
+        }
+      }
+      if (half == 0) a.lse[qrow] = live ? lse2 * kLn2 : -__builtin_inff();
+    }
+  } else {
+    const int64_t rec =
+        (((int64_t)split * a.num_groups + group) * a.row_blocks + rb) * kWaves + wave;
+    float* dst = a.ws_o + rec * kRecFloats;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        f32x4 v = {o[db][4 * qq + 0] * inv, o[db][4 * qq + 1] * inv, o[db][4 * qq + 2] * inv,
+                   o[db][4 * qq + 3] * inv};
+        *reinterpret_cast<f32x4*>(dst + ((db * 4 + qq) * 64 + lane) * 4) = v;
+      }
+    }
+    if (half == 0) a.ws_lse[rec * kRowsPerWave + l32] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine kernel: lse = log2 sum_s 2^{lse_s}; out = sum_s 2^{lse_s - lse} o_s.
+// One thread per 4 consecutive output dims of one row. A wave record (32 rows
+// x 512 dims = 4096 float4) is covered by 16 blocks of 256 threads.
+// ---------------------------------------------------------------------------
+static_assert(16 * 256 * 4 == kRecFloats, "16 combine blocks of 256 float4 cover one wave record");
+
+template <int MODE>
+__global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
+  constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
+  const int bid = blockIdx.x;
+  const int part = bid & 15;
+  const int wrec = bid >> 4;
+  const int wave = wrec & 3;
+  const int rbg = wrec >> 2;
+  const int rb = rbg % a.row_blocks;
+  const int group = rbg / a.row_blocks;
+
+  const int idx = part * 256 + threadIdx.x;  // 0..4095
+  const int lane = idx & 63;
+  const int qq = (idx >> 6) & 3;
+  const int db = idx >> 8;                    // 0..15
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
+  if (row >= a.rows_per_group) return;
+  const int64_t qrow = (int64_t)group * a.rows_per_group + row;
+
+  const GroupInfo gi = group_info(a, group, kSparseMode);
+  const int n_active = min(a.num_splits, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
+  const int64_t rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
+  const int64_t rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
+
+  float mx = -__builtin_inff();
+  for (int s = 0; s < n_active; ++s)
+    mx = fmaxf(mx, a.ws_lse[(rec0 + s * rec_stride) * kRowsPerWave + l32]);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx != -__builtin_inff()) {
+    for (int s = 0; s < n_active; ++s) {
+      const int64_t rec = rec0 + s * rec_stride;
+      const float ls = a.ws_lse[rec * kRowsPerWave + l32];
+      if (ls == -__builtin_inff()) continue;
+      const float w = fast_exp2(ls - mx);
+      wsum += w;
+      const f32x4 v =
+          *reinterpret_cast<const f32x4*>(a.ws_o + rec * kRecFloats + ((db * 4 + qq) * 64 + lane) * 4);
+      acc += w * v;
+    }
+  }
+  const bool live = wsum > 0.f;
+  const float inv = live ? 1.0f / wsum : 0.f;
+  const int d = db * 32 + 8 * qq + 4 * half;
+  uint2 pkd;
+  pkd.x = (uint32_t)bf16_bits(acc[0] * inv) | ((uint32_t)bf16_bits(acc[1] * inv) << 16);
+  pkd.y = (uint32_t)bf16_bits(acc[2] * inv) | ((uint32_t)bf16_bits(acc[3] * inv) << 16);
+  *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
+  if (db == 0 && qq == 0 && half == 0)
+    a.lse[qrow] = live ? (mx + fast_log2(wsum)) * kLn2 : -__builtin_inff();
+}
+
+// ---------------------------------------------------------------------------
+template <int MODE>
+static hipError_t launch_split(const MainArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)a.row_blocks * (unsigned)a.num_splits * (unsigned)a.num_groups;
+  hipLaunchKernelGGL(mla_split_kernel<MODE>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_combine(const MainArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)a.num_groups * (unsigned)a.row_blocks * kWaves * 16u;
+  hipLaunchKernelGGL(mla_combine_kernel<MODE>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_kernel(const MainArgs& a, int mode, hipStream_t s) {
+  switch (mode) {
+    case kContig: return launch_split<kContig>(a, s);
+    case kPaged: return launch_split<kPaged>(a, s);
+    case kSparse: return launch_split<kSparse>(a, s);
+    case kSparsePaged: return launch_split<kSparsePaged>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine_kernel(const MainArgs& a, int mode, hipStream_t s) {
+  switch (mode) {
+    case kContig: return launch_combine<kContig>(a, s);
+    case kPaged: return launch_combine<kPaged>(a, s);
+    case kSparse: return launch_combine<kSparse>(a, s);
+    case kSparsePaged: return launch_combine<kSparsePaged>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mlav

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments with the documented codes before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import speculative_decode_verify_mla_amd as mv
+from speculative_decode_verify_mla_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmla_verify.so is not built (run __graft_entry__.build())")
+    return mv.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mla_\w+)\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def _dims(**kw):
+    base = dict(batch=1, num_q=4, num_heads=16, max_kv_len=132, kv_rows=132, kv_seq_stride=132)
+    base.update(kw)
+    return B.make_dims(**base)
+
+
+class FakePtr:
+    """Aligned non-NULL addresses that are never dereferenced (validation fails first)."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def __call__(self):
+        return ctypes.c_void_p(self.addr)
+
+
+P = FakePtr(0x10000)
+MIS = FakePtr(0x10002)
+
+
+def call(lib, dims, sparse=False, ptrs=None, ws=None, ws_bytes=0, scale=0.1):
+    p = dict(q_lat=P(), q_rope=P(), c_kv=P(), k_rope=P(), pt=None, mask=None, idx=P(),
+             kv_lens=P(), out=P(), lse=P())
+    if ptrs:
+        p.update(ptrs)
+    fn = lib.mla_sparse_attn if sparse else lib.mla_verify_attn
+    third = p["idx"] if sparse else p["mask"]
+    return fn(ctypes.byref(dims) if dims is not None else None, p["q_lat"], p["q_rope"],
+              p["c_kv"], p["k_rope"], p["pt"], third, p["kv_lens"], ctypes.c_float(scale),
+              p["out"], p["lse"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case", [
+    dict(dims=None),
+    dict(kw=dict(num_q=0)),
+    dict(kw=dict(num_q=65)),
+    dict(kw=dict(batch=0)),
+    dict(kw=dict(num_heads=0)),
+    dict(kw=dict(max_kv_len=3)),            # max_kv_len < T
+    dict(kw=dict(kv_seq_stride=100)),       # stride < max_kv_len
+    dict(kw=dict(batch=2)),                 # second sequence past kv_rows
+    dict(kw=dict(num_splits=-1)),
+    dict(kw=dict(phase=3)),
+    dict(ptrs=dict(q_lat=None)),
+    dict(ptrs=dict(out=None)),
+    dict(ptrs=dict(kv_lens=None)),
+    dict(ptrs=dict(c_kv=MIS())),            # misaligned
+    dict(ptrs=dict(pt=P())),                # page table without page size
+    dict(kw=dict(page_size=64, max_pages=3)),  # page size without page table
+    dict(kw=dict(page_size=32, max_pages=5), ptrs=dict(pt=P())),  # not a multiple of 64
+    dict(kw=dict(page_size=64, max_pages=2), ptrs=dict(pt=P())),  # 2*64 < max_kv_len
+    dict(scale=float("nan")),
+])
+def test_invalid_arguments(lib, case):
+    dims = None if "dims" in case else _dims(**case.get("kw", {}))
+    rc = call(lib, dims, ptrs=case.get("ptrs"), scale=case.get("scale", 0.1))
+    assert rc == B.MLA_ERR_INVALID
+
+
+def test_reserved_must_be_zero(lib):
+    d = _dims()
+    d.reserved = 1
+    assert call(lib, d) == B.MLA_ERR_INVALID
+
+
+def test_sparse_invalid(lib):
+    d = _dims(topk=0, num_q=1)
+    assert call(lib, d, sparse=True) == B.MLA_ERR_INVALID
+    d = _dims(topk=16, num_q=1)
+    assert call(lib, d, sparse=True, ptrs=dict(idx=None)) == B.MLA_ERR_INVALID
+    big = (1 << 21) + 64
+    d = _dims(topk=16, num_q=1, max_kv_len=big, kv_rows=big, kv_seq_stride=big)
+    assert call(lib, d, sparse=True) == B.MLA_ERR_INVALID
+
+
+def test_workspace_too_small(lib):
+    d = _dims(num_q=16, num_heads=64, max_kv_len=65552, kv_rows=65552, kv_seq_stride=65552)
+    need = mv.workspace_bytes(d)
+    assert need > 0
+    assert call(lib, d) == B.MLA_ERR_WORKSPACE
+    assert call(lib, d, ws=ctypes.c_void_p(0x100000), ws_bytes=need - 1) == B.MLA_ERR_WORKSPACE
+    assert call(lib, d, ws=ctypes.c_void_p(0x100008), ws_bytes=need) == B.MLA_ERR_WORKSPACE
+
+
+def test_plan_shapes():
+    # long-prefix verify: 8 row blocks x 32 splits = one workgroup per CU on 256 CUs
+    d = _dims(num_q=16, num_heads=64, max_kv_len=65552, kv_rows=65552, kv_seq_stride=65552)
+    p = mv.plan(d)
+    assert (p.row_blocks, p.num_groups, p.rows_per_group) == (8, 1, 1024)
+    assert p.num_splits * p.chunk_tiles >= 1025 > (p.num_splits - 1) * p.chunk_tiles
+    assert p.workspace_bytes == p.num_splits * 8 * 4 * (32 * 512 * 4 + 32 * 4)
+    # tiny chain: one split, no workspace
+    p1 = mv.plan(_dims())
+    assert p1.num_splits == 1 and p1.workspace_bytes == 0
+    # sparse decode: groups are tokens, rows are heads
+    d5 = _dims(batch=32, num_q=1, num_heads=64, topk=2048, max_kv_len=131072,
+               kv_rows=32 * 131072, kv_seq_stride=131072)
+    p5 = mv.plan(d5, sparse=True)
+    assert (p5.num_groups, p5.rows_per_group, p5.row_blocks) == (32, 64, 1)
+    # requested splits are honoured when they divide the tiles evenly, else rounded down
+    p5b = mv.plan(_dims(num_splits=7, max_kv_len=640, kv_rows=640, kv_seq_stride=640))
+    assert (p5b.num_splits, p5b.chunk_tiles) == (5, 2)
+    p7 = mv.plan(_dims(num_splits=7, max_kv_len=896, kv_rows=896, kv_seq_stride=896))
+    assert p7.num_splits == 7 and p7.chunk_tiles == 2
+    p8 = mv.plan(_dims(num_splits=50))
+    assert p8.num_splits == 3  # 132 keys = 3 tiles
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, 99):
+        assert isinstance(lib.mla_verify_strerror(code), bytes)
+    assert mv.strerror(B.MLA_ERR_WORKSPACE) == "workspace missing or too small"

@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: |out - oracle|_inf <= 1e-2 (bf16 output) and |lse - oracle|_inf <= 1e-3.
+Every case prints its name, seed and shape before touching the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decode_verify_mla_amd as mv
+from speculative_decode_verify_mla_amd import synth
+from speculative_decode_verify_mla_amd.synth import Spec, generate
+from tests._util import run_oracle, oracle_inputs
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+def _announce(tag, w):
+    print(f"[case] {tag} seed={w.seed} B={w.B} T={w.T} H={w.H} layout={w.layout} "
+          f"kv_lens={w.kv_lens.tolist()[:8]} topk={w.topk}", flush=True)
+
+
+def _dev(w):
+    from tests._gpu import DeviceWorkload
+    return DeviceWorkload(w)
+
+
+def _check(out, lse, ref_out, ref_lse, tag=""):
+    assert np.isfinite(out).all(), f"{tag}: non-finite output"
+    assert np.isfinite(lse).all(), f"{tag}: non-finite lse"
+    e_out = np.abs(out - ref_out).max()
+    e_lse = np.abs(lse - ref_lse).max()
+    rel = math.sqrt(((out - ref_out) ** 2).mean() / max(((ref_out) ** 2).mean(), 1e-300))
+    print(f"   {tag}: max|dout|={e_out:.3e} max|dlse|={e_lse:.3e} rel_rms(out)={rel:.3e}", flush=True)
+    assert e_out <= OUT_TOL, f"{tag}: out error {e_out}"
+    assert e_lse <= LSE_TOL, f"{tag}: lse error {e_lse}"
+
+
+SMALL = [
+    Spec("contig_ragged_rows", B=2, T=5, H=40, layout="contig", prefix=[300, 777]),
+    Spec("contig_chain_h16", B=1, T=4, H=16, layout="contig", prefix=1000, tree="chain",
+         pass_null_mask=True),
+    Spec("contig_t64", B=1, T=64, H=8, layout="contig", prefix=200),
+    Spec("contig_t1", B=3, T=1, H=64, layout="contig", prefix=[5, 64, 4000]),
+    Spec("paged_small", B=3, T=8, H=64, layout="paged", prefix=[100, 1000, 3000]),
+    Spec("paged_p128", B=2, T=3, H=32, layout="paged", prefix=[700, 190], page_size=128),
+    Spec("sparse_small", B=4, T=2, H=64, layout="sparse", cache_len=5000, topk=300),
+    Spec("sparse_h32_k70", B=2, T=3, H=32, layout="sparse", cache_len=900, topk=70),
+    Spec("sparse_paged", B=2, T=2, H=64, layout="sparse", cache_len=3000, topk=200,
+         paged_sparse=True),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_small_parity(gpu_lib, spec, splits):
+    w = generate(spec, seed=7)
+    _announce(f"{spec.name} splits={splits}", w)
+    ref = run_oracle(w)
+    d = _dev(w)
+    d.run(num_splits=splits)
+    _check(*d.results(), *ref, tag=spec.name)
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_config_parity(gpu_lib, i):
+    w = synth.config(i)
+    _announce(f"config{i}", w)
+    d = _dev(w)
+    d.run()
+    out, lse = d.results()
+    ref = run_oracle(w)
+    _check(out, lse, *ref, tag=f"config{i}")
+
+
+def test_paged_poison_does_not_leak(gpu_lib):
+    spec = Spec("poison", B=3, T=8, H=64, layout="paged", prefix=[100, 1000, 2500])
+    w = generate(spec, seed=11, poison=True)
+    _announce("paged poison", w)
+    d = _dev(w)
+    d.run()
+    _check(*d.results(), *run_oracle(w), tag="poison")
+
+
+def test_contig_poison_past_kv_len(gpu_lib):
+    spec = Spec("ragged_poison", B=3, T=4, H=64, layout="contig", prefix=[70, 1500, 300])
+    w = generate(spec, seed=12, poison=True)
+    _announce("contig poison", w)
+    d = _dev(w)
+    d.run()
+    _check(*d.results(), *run_oracle(w), tag="contig_poison")
+
+
+def test_single_key_is_exact(gpu_lib):
+    """kv_len = 1, T = 1: out equals the c_kv row bit for bit; lse is the lone score."""
+    spec = Spec("one", B=1, T=1, H=64, layout="contig", prefix=0)
+    w = generate(spec, seed=13)
+    _announce("single key", w)
+    d = _dev(w)
+    d.run()
+    out, lse = d.results()
+    row = synth.bf16_bits_to_f64(w.c_kv[0])
+    assert np.array_equal(out[0, 0], np.broadcast_to(row, out[0, 0].shape))
+    _check(out, lse, *run_oracle(w), tag="single")
+
+
+def test_uniform_scores_give_mean(gpu_lib):
+    spec = Spec("uni", B=1, T=6, H=64, layout="contig", prefix=333)
+    w = generate(spec, seed=14)
+    w.q_lat[:] = 0
+    w.q_rope[:] = 0
+    _announce("uniform", w)
+    d = _dev(w)
+    d.run()
+    out, lse = d.results()
+    ref_out, ref_lse = run_oracle(w)
+    _check(out, lse, ref_out, ref_lse, tag="uniform")
+    P = int(w.kv_lens[0]) - w.T
+    for t in range(w.T):
+        n = P + int(w.tree_mask[0, t].sum())
+        assert np.abs(lse[0, t] - math.log(n)).max() < 1e-5
+
+
+def test_splits_agree(gpu_lib):
+    spec = Spec("splits", B=1, T=8, H=64, layout="contig", prefix=3000)
+    w = generate(spec, seed=15)
+    _announce("splits agree", w)
+    d = _dev(w)
+    res = []
+    for s in (1, 2, 3, 7, 0):
+        d.run(num_splits=s)
+        res.append(d.results())
+    ref = run_oracle(w)
+    for o, l in res:
+        _check(o, l, *ref, tag="split")
+        assert np.abs(l - res[0][1]).max() < 2e-4
+
+
+def test_paged_equals_contiguous_bitwise(gpu_lib):
+    """Split boundaries are logical positions, so paging must not change a single bit."""
+    spec = Spec("pg", B=2, T=8, H=64, layout="paged", prefix=[900, 2000])
+    w = generate(spec, seed=16)
+    _announce("paged vs contiguous", w)
+    d = _dev(w)
+    d.run(num_splits=4)
+    o_p, l_p = d.results()
+    stride = int(w.kv_lens.max())
+    c = np.zeros((w.B * stride, 512), np.uint16)
+    k = np.zeros((w.B * stride, 64), np.uint16)
+    for b in range(w.B):
+        for p in range(int(w.kv_lens[b])):
+            r = int(w.page_table[b, p // 64]) * 64 + p % 64
+            c[b * stride + p], k[b * stride + p] = w.c_kv[r], w.k_rope[r]
+    import dataclasses
+    wc = dataclasses.replace(w, layout="contig", c_kv=c, k_rope=k, kv_rows=w.B * stride,
+                             kv_seq_stride=stride, page_table=None, page_size=0,
+                             spec=dataclasses.replace(spec, layout="contig"))
+    dc = _dev(wc)
+    dc.run(num_splits=4)
+    o_c, l_c = dc.results()
+    assert np.array_equal(o_p, o_c) and np.array_equal(l_p, l_c)
+
+
+def test_sparse_arange_matches_dense(gpu_lib):
+    spec = Spec("dense1", B=2, T=1, H=64, layout="contig", prefix=[1000, 1500])
+    w = generate(spec, seed=17)
+    _announce("sparse arange vs dense", w)
+    d = _dev(w)
+    d.run(num_splits=1)
+    o_d, l_d = d.results()
+    K = int(w.kv_lens.max())
+    idx = np.full((2, 1, K), -1, np.int32)
+    for b in range(2):
+        idx[b, 0, : w.kv_lens[b]] = np.arange(w.kv_lens[b])
+    d.indices = torch.from_numpy(idx).to(d.device)
+    import dataclasses
+    d.w = dataclasses.replace(w, layout="sparse", indices=idx, topk=K)
+    d.run(num_splits=1)
+    o_s, l_s = d.results()
+    assert np.abs(o_s - o_d).max() <= 2 ** -8 * max(np.abs(o_d).max(), 1e-3)
+    assert np.abs(l_s - l_d).max() < 1e-5
+
+
+def test_deterministic(gpu_lib):
+    w = synth.config(2)
+    _announce("determinism", w)
+    d = _dev(w)
+    d.run()
+    a = d.results()
+    d.run()
+    b = d.results()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_phases_equal_one_call(gpu_lib):
+    spec = Spec("ph", B=2, T=4, H=64, layout="contig", prefix=[2000, 4000])
+    w = generate(spec, seed=18)
+    _announce("phases", w)
+    d = _dev(w)
+    d.run(num_splits=5)
+    a = d.results()
+    d.out.zero_()
+    d.lse.zero_()
+    d.run(num_splits=5, phase=mv.binding.PHASE_PARTIAL)
+    d.run(num_splits=5, phase=mv.binding.PHASE_COMBINE)
+    b = d.results()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_late_large_score_takes_exact_second_pass(gpu_lib):
+    """A key far past the first tile scores ~100 nats above the rest: the result is
+    that key's row (argmax limit), reached through the split's exact second pass."""
+    spec = Spec("argmax", B=1, T=2, H=64, layout="contig", prefix=900)
+    w = generate(spec, seed=19)
+    j = 700
+    kv = synth.bf16_bits_to_f32(w.c_kv[j])
+    # q = c * c_kv[j] for every head of token 0: score about c*|c_kv[j]|^2*scale
+    c = 100.0 / (float(kv.astype(np.float64) @ kv) * w.scale)
+    w.q_lat[0, 0, :] = synth.f32_to_bf16_bits(np.broadcast_to(c * kv, (w.H, 512)).copy())
+    _announce("late large score", w)
+    d = _dev(w)
+    for s in (1, 0):
+        d.run(num_splits=s)
+        out, lse = d.results()
+        ref_out, ref_lse = run_oracle(w)
+        _check(out, lse, ref_out, ref_lse, tag=f"argmax splits={s}")
+        assert np.abs(out[0, 0] - synth.bf16_bits_to_f64(w.c_kv[j])).max() < 1e-2
