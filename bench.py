@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic plan")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device-to-device copy (hardware counter scale)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -166,8 +168,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    mv.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # A copy kernel of known size: 256 MiB read + 256 MiB written per launch.
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 launches of a 268435456-byte device copy")
+        return
+    mv.load_library()
     log(f"device {torch.cuda.get_device_name(0)}; workload config {args.config}")
 
     w = synth.config(args.config)

@@ -133,7 +133,8 @@ size_t mla_verify_workspace_bytes(const mla_dims* dims, int sparse);
 /* Dense tree-verify attention (see the file comment for the operation).
  * Checks (MLA_ERR_INVALID): dims, q_lat, q_rope, c_kv, k_rope, kv_lens, out,
  * lse non-NULL; bf16 arrays 16-byte aligned, lse/kv_lens/page_table 4-byte
- * aligned; B >= 1, 1 <= T <= 64, H >= 1; T <= max_kv_len; num_splits >= 0;
+ * aligned; scale finite and > 0; B >= 1, 1 <= T <= 64, H >= 1;
+ * T <= max_kv_len; num_splits >= 0;
  * phase valid; reserved == 0; contiguous: page_table NULL, page_size 0,
  * kv_seq_stride >= max_kv_len and (B-1)*kv_seq_stride + max_kv_len <= kv_rows;
  * paged: page_table non-NULL, page_size a positive multiple of 64,

@@ -132,7 +132,8 @@ int run(const mla_dims* d, bool sparse, const uint16_t* q_lat, const uint16_t* q
     return MLA_ERR_INVALID;
   if ((page_table && !aligned(page_table, 4)) || (indices && !aligned(indices, 4)))
     return MLA_ERR_INVALID;
-  if (!(scale == scale)) return MLA_ERR_INVALID;  // NaN scale
+  // softmax scale: finite and positive (masked keys are -inf scores)
+  if (!(scale > 0.0f) || !(scale < __builtin_inff())) return MLA_ERR_INVALID;
   mla_plan_info p;
   rc = make_plan(d, sparse, &p);
   if (rc != MLA_OK) return rc;

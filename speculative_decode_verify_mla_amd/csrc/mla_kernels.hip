@@ -40,6 +40,7 @@ namespace mlav {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -59,6 +60,12 @@ constexpr unsigned kBufferConfig = 0x00020000u;  // raw buffer, 32-bit data form
 constexpr unsigned kOobOffset = 0x80000000u;     // an offset every range check rejects
 constexpr float kOverflowLog2 = 32.0f;           // largest exponent (log2 units) a term may take
 constexpr float kLn2 = 0.69314718055994530942f;
+// LDS fragments in flight ahead of the MFMA that consumes them: one wave per
+// SIMD leaves nothing else to cover the LDS latency.
+#ifndef MLA_FRAG_AHEAD
+#define MLA_FRAG_AHEAD 2
+#endif
+constexpr int kFragAhead = MLA_FRAG_AHEAD;
 
 // ---------------------------------------------------------------------------
 // LDS swizzles. A tile is stored row-major (key-major) with its 16-byte chunks
@@ -112,16 +119,16 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // reading the result with VALU needs the wait states of score_fence().
 __device__ __forceinline__ f32x16 mfma32_v_first(bf16x8 a, bf16x8 b) {
   f32x16 d;
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
   return d;
 }
 __device__ __forceinline__ void mfma32_v_acc(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 // Independent-instruction wait states between the last score MFMA and any
 // VALU/VMEM/LDS access of its result (more than a 16-pass XDL op requires).
-__device__ __forceinline__ void score_fence(f32x16& s0, f32x16& s1) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+__device__ __forceinline__ void score_fence(f32x16& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -225,28 +232,25 @@ mla_split_kernel(MainArgs a) {
   }
 
   // ---- per-lane LDS read offsets ------------------------------------------
-  // S^T operand: key = kb*32 + l32, logical chunk 2c + half; the XOR swizzle
-  // acts on the low 4 chunk bits, so 8 offsets cover the 32 latent chunks and
-  // (c >> 3) * 256 is an immediate.
+  // The swizzle XORs chunk-index bits that lie below a key row's base offset,
+  // so every fragment offset is one per-lane base XOR a compile-time constant.
+  // S^T operand (K rows): key = kb*32 + l32, logical 16-byte chunk 2c + half:
+  //   offset = (l32*1024 + 16*(half ^ swz(l32))) ^ (32*(c%8)) + 256*(c/8) + kb*32768.
   const int xlat = half ^ swz_lat(l32);
   const int yrope = half ^ swz_rope(l32);
-  unsigned offA[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) offA[j] = l32 * 1024 + (((2 * j) ^ xlat) * 16);
+  const unsigned kbaseA = (unsigned)(l32 * 1024 + 16 * xlat);
   // V^T operand through the transposing read: within each 16-lane group G,
   // lane i addresses key (base + i/4) and 4 dims starting at 4*(i%4); the
-  // hardware hands lane i the 4 keys of dim i. Two reads cover 8 keys.
-  unsigned offV[2][4];
+  // hardware hands lane i the 4 keys of dim i. Two reads (keys +0 and +8) make
+  // one 8-key operand: offset = vbase[second] ^ (64*(db%4)) + 256*(db/4) + 16384*kc.
+  unsigned vbase[2];
   {
     const int G = lane >> 4, i = lane & 15, h = lane >> 5;
     const int u = 2 * (G & 1) + ((i & 3) >> 1);
 #pragma unroll
     for (int second = 0; second < 2; ++second) {
       const int key = 8 * second + 4 * h + (i >> 2);
-      const int sw = swz_lat(key);
-#pragma unroll
-      for (int dq = 0; dq < 4; ++dq)
-        offV[second][dq] = key * 1024 + ((((4 * dq) | u) ^ sw) * 16) + 8 * (i & 1);
+      vbase[second] = (unsigned)(key * 1024 + 16 * (u ^ swz_lat(key)) + 8 * (i & 1));
     }
   }
 
@@ -335,16 +339,90 @@ mla_split_kernel(MainArgs a) {
 
   // ---- softmax state ------------------------------------------------------------
   // The accumulator is never rescaled inside the loop: every exponent is taken
-  // against a fixed per-row reference m_ref (the row max of the first tile with
-  // a visible key). If a later score exceeds m_ref by more than 2^32 (log2
-  // units), the split is run a second time with m_ref = the true row max, so
-  // no exponent ever exceeds 2^32 and the result is exact either way.
+  // against a fixed per-row reference m_ref (the row max of the first half-tile
+  // with a visible key). A half-tile whose row sum reaches 2^32 (some score more
+  // than 32 log2-units above m_ref) marks the split for a second pass, run with
+  // a reference raised to the largest score seen there, so no term ever exceeds
+  // 2^32 and the result is exact either way.
   f32x16 o[16];
   float m_ref = -__builtin_inff();   // log2 domain; equal in both lanes of a row
-  float m_true = -__builtin_inff();  // this lane's max over every visible score
+  float m_hi = -__builtin_inff();    // largest score of half-tiles that overflowed
   float l_run = 0.f;                 // this lane's share of the row sum (fp32 terms: the lse)
   float lq_run = 0.f;                // the same sum over the bf16-rounded terms fed to PV
   int* restart_flag = reinterpret_cast<int*>(smem + kLdsBytes);
+  const float c2 = a.scale_log2;
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // Visibility of the tile's 64 keys for this lane's row (bit = key), and of the
+  // lane's 16 keys of half `kb` (bit r <-> accumulator register r, which holds
+  // key 32kb + 8(r/4) + 4*half + r%4).
+  auto tile_visibility = [&](int pos0, int nv, uint64_t vm) -> uint64_t {
+    if (kSparseMode) return vm;
+    const uint64_t valid = nv >= 64 ? ~0ull : ((1ull << nv) - 1ull);
+    const int d = prefix - pos0;  // tile-relative position of draft 0
+    const uint64_t pre = d <= 0 ? 0ull : (d >= 64 ? ~0ull : ((1ull << d) - 1ull));
+    const uint64_t drafts = d >= 64 ? 0ull : (d >= 0 ? (vis << d) : (d <= -64 ? 0ull : (vis >> -d)));
+    return valid & (pre | drafts);
+  };
+  auto half_bits = [&](uint64_t tv, int kb) -> uint32_t {
+    const uint32_t w = (uint32_t)(tv >> (32 * kb + 4 * half));
+    return (w & 0xFu) | ((w >> 4) & 0xF0u) | ((w >> 8) & 0xF00u) | ((w >> 12) & 0xF000u);
+  };
+  // Row max (log2 units) of a half's raw scores (masked ones are -inf), both lanes of the row.
+  auto half_row_max = [&](const f32x16& s) -> float {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx *= c2;
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
+  // Score chain of half `kb` (keys 32kb .. 32kb+31) with a VALU slice `work(c)`
+  // placed after each of its 36 MFMAs; K fragments are read one step ahead.
+  auto score_chain = [&](const uint8_t* sb, int kb, auto&& work) -> f32x16 {
+    // opaque copy: keeps the compiler from hoisting the 8 XORed offsets into registers
+    unsigned kbase = kbaseA;
+    asm volatile("" : "+v"(kbase));
+    auto k_off = [&](int c) -> unsigned {
+      return c < 32 ? (kbase ^ (unsigned)(32 * (c & 7))) + (unsigned)((c >> 3) * 256 + kb * 32 * 1024)
+                    : (unsigned)(kLatBytes + (l32 + 32 * kb) * 128 + (((2 * (c - 32)) ^ yrope) * 16));
+    };
+    f32x16 acc;
+    bf16x8 kf[kFragAhead];
+#pragma unroll
+    for (int j = 0; j < kFragAhead; ++j) kf[j] = lds_read16(sb, k_off(j));
+#pragma unroll
+    for (int c = 0; c < 36; ++c) {
+      if (c == 0) acc = mfma32_v_first(kf[0], q[0]);
+      else mfma32_v_acc(acc, kf[c % kFragAhead], q[c]);
+      if (c + kFragAhead < 36) kf[c % kFragAhead] = lds_read16(sb, k_off(c + kFragAhead));
+      work(c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    score_fence(acc);
+    return acc;
+  };
+  // One slice of the softmax of a half: steps 0..15 exponentiate term `step`
+  // (in place), steps 16..23 pack two terms to bf16 and add them to the rounded sum.
+  auto softmax_step = [&](int step, f32x16& s, float m_use, float& psum, float& qsum,
+                          bf16x8* pk) {
+    if (step < 16) {
+      const float p = fast_exp2(__builtin_fmaf(s[step], c2, -m_use));
+      psum += p;
+      s[step] = p;
+    } else if (step < 24) {
+      const int j = step - 16;
+      const bf16x2 b2 = {(__bf16)s[2 * j], (__bf16)s[2 * j + 1]};
+      qsum = __builtin_amdgcn_fdot2_f32_bf16(b2, ones2, qsum, false);
+      pk[j >> 2][2 * (j & 3)] = b2[0];
+      pk[j >> 2][2 * (j & 3) + 1] = b2[1];
+    }
+  };
+  auto init_reference = [&](const f32x16& s) {
+    if (__ballot(m_ref == -__builtin_inff()) != 0ull) {
+      const float mx = half_row_max(s);
+      m_ref = m_ref == -__builtin_inff() ? mx : m_ref;
+    }
+  };
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -384,110 +462,68 @@ mla_split_kernel(MainArgs a) {
 
       if (wave_active) {
         const uint8_t* sb = smem + stage * kStageBytes;
-        // -- S^T = K Q^T over 576 dims: two 32-key blocks ------------------------
-        // K fragments are read one 16-dim step ahead of the MFMAs that use them.
-        auto k_off = [&](int c) -> unsigned {
-          return c < 32 ? offA[c & 7] + (unsigned)((c >> 3) * 256)
-                        : (unsigned)(kLatBytes + l32 * 128 + (((2 * (c - 32)) ^ yrope) * 16));
-        };
-        auto k_blk = [&](int c) -> unsigned { return c < 32 ? 32u * 1024u : 32u * 128u; };
-        f32x16 s0, s1;
-        bf16x8 ka0 = lds_read16(sb, k_off(0));
-        bf16x8 ka1 = lds_read16(sb, k_off(0) + k_blk(0));
-#pragma unroll
-        for (int c = 0; c < 36; ++c) {
-          bf16x8 kb0 = ka0, kb1 = ka1;
-          if (c + 1 < 36) {
-            kb0 = lds_read16(sb, k_off(c + 1));
-            kb1 = lds_read16(sb, k_off(c + 1) + k_blk(c + 1));
-          }
-          if (c == 0) {
-            s0 = mfma32_v_first(ka0, q[c]);
-            s1 = mfma32_v_first(ka1, q[c]);
-          } else {
-            mfma32_v_acc(s0, ka0, q[c]);
-            mfma32_v_acc(s1, ka1, q[c]);
-          }
-          ka0 = kb0;
-          ka1 = kb1;
-        }
-        score_fence(s0, s1);
-
-        // -- scale into log2 units and mask ---------------------------------------
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s0[r] *= a.scale_log2;
-          s1[r] *= a.scale_log2;
-        }
         const int pos0 = tile * kTile;
-        const bool need_mask = kSparseMode ? (vm_cur != ~0ull)
-                                           : (nv_cur < kTile || pos0 + kTile > prefix);
-        if (need_mask) {
+        // Tiles holding absent or invisible keys (sequence tail, draft keys,
+        // sparse gaps) set those raw scores to -inf (scale > 0 keeps them -inf).
+        const bool masked = kSparseMode ? (vm_cur != ~0ull)
+                                        : (nv_cur < kTile || pos0 + kTile > prefix);
+        auto apply_mask = [&](f32x16& sc, int kb) {
+          if (masked) {
+            const uint32_t bits = half_bits(tile_visibility(pos0, nv_cur, vm_cur), kb);
 #pragma unroll
-          for (int r = 0; r < 32; ++r) {
-            // accumulator register r%16 of block r/16 holds key 8*((r%16)/4) + 4*half + r%4
-            const int key = 32 * (r >> 4) + 8 * ((r & 15) >> 2) + 4 * half + (r & 3);
-            bool ok;
-            if (kSparseMode) {
-              ok = (vm_cur >> key) & 1ull;
-            } else {
-              const int p = pos0 + key;
-              ok = key < nv_cur && (p < prefix || ((vis >> ((p - prefix) & 63)) & 1ull));
-            }
-            if (r < 16) s0[r] = ok ? s0[r] : -__builtin_inff();
-            else s1[r - 16] = ok ? s1[r - 16] : -__builtin_inff();
+            for (int r = 0; r < 16; ++r) sc[r] = ((bits >> r) & 1u) ? sc[r] : -__builtin_inff();
           }
-        }
-
-        // -- reference max and overflow check --------------------------------------
-        float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        m_true = fmaxf(m_true, mx);
-        if (__ballot(m_ref == -__builtin_inff() && mx != -__builtin_inff()) != 0ull) {
-          // first visible keys of some row: its reference is this tile's row max
-          // (its accumulator and sum are still zero, so nothing is rescaled)
-          const float row_mx = fmaxf(mx, __shfl_xor(mx, 32));
-          m_ref = m_ref == -__builtin_inff() ? row_mx : m_ref;
-        }
-        overflow = overflow || (mx > m_ref + kOverflowLog2);
-        const float m_use = m_ref == -__builtin_inff() ? 0.f : m_ref;
-
-        // -- P = 2^(s - m_ref), row sums, bf16 operand for the PV product -------------
-        // The output is normalised by the sum of the rounded terms it actually
-        // accumulated (an exact convex combination of value rows); the lse uses
-        // the fp32 terms.
-        float psum = 0.f, qsum = 0.f;
+        };
+        float psa = 0.f, qsa = 0.f, psb = 0.f, qsb = 0.f;
         bf16x8 pk[4];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p0 = fast_exp2(fminf(s0[r] - m_use, kOverflowLog2));
-          const float p1 = fast_exp2(fminf(s1[r] - m_use, kOverflowLog2));
-          const __bf16 b0 = (__bf16)p0, b1 = (__bf16)p1;
-          psum += p0 + p1;
-          qsum += (float)b0 + (float)b1;
-          pk[r >> 3][r & 7] = b0;
-          pk[2 + (r >> 3)][r & 7] = b1;
-        }
-        l_run += psum;
-        lq_run += qsum;
 
-        // -- O^T += V^T P^T: 16 blocks of 32 dims x 4 steps of 16 keys -------------
-        // V^T fragments are read one step ahead of the MFMA that uses them.
+        // -- S_a: scores of keys 0..31 ----------------------------------------------
+        f32x16 sa = score_chain(sb, 0, [](int) {});
+        apply_mask(sa, 0);
+        init_reference(sa);
+        const float mu_a = m_ref == -__builtin_inff() ? 0.f : m_ref;
+
+        // -- S_b on the matrix cores while the VALU exponentiates S_a ---------------
+        f32x16 sbk = score_chain(sb, 1, [&](int c) { softmax_step(c, sa, mu_a, psa, qsa, pk); });
+        apply_mask(sbk, 1);
+        init_reference(sbk);
+        const float mu_b = m_ref == -__builtin_inff() ? 0.f : m_ref;
+
+        // -- O^T += V^T P^T over keys 0..31 while the VALU exponentiates S_b; then
+        //    keys 32..63. Step = (16-key chunk kc) x (32-dim block db); V^T
+        //    fragments are read one step ahead. -----------------------------------
+        unsigned vb0 = vbase[0], vb1 = vbase[1];
+        asm volatile("" : "+v"(vb0), "+v"(vb1));  // see score_chain
         auto v_frag = [&](int step) -> bf16x8 {
-          const int db = step >> 2, kc = step & 3;
+          const int kc = step >> 4, db = step & 15;
           const unsigned hi = (unsigned)((db >> 2) * 256 + kc * 16384);
-          const bf16x4 v0 = lds_read_tr(sb, offV[0][db & 3] + hi);
-          const bf16x4 v1 = lds_read_tr(sb, offV[1][db & 3] + hi);
+          const bf16x4 v0 = lds_read_tr(sb, (vb0 ^ (unsigned)(64 * (db & 3))) + hi);
+          const bf16x4 v1 = lds_read_tr(sb, (vb1 ^ (unsigned)(64 * (db & 3))) + hi);
           return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         };
-        bf16x8 va = v_frag(0);
+        bf16x8 vf[kFragAhead];
+#pragma unroll
+        for (int j = 0; j < kFragAhead; ++j) vf[j] = v_frag(j);
 #pragma unroll
         for (int step = 0; step < 64; ++step) {
-          bf16x8 vb = va;
-          if (step + 1 < 64) vb = v_frag(step + 1);
-          o[step >> 2] = mfma32(va, pk[step & 3], o[step >> 2]);
-          va = vb;
+          o[step & 15] = mfma32(vf[step % kFragAhead], pk[step >> 4], o[step & 15]);
+          if (step + kFragAhead < 64) vf[step % kFragAhead] = v_frag(step + kFragAhead);
+          if (step < 32) softmax_step(step, sbk, mu_b, psb, qsb, pk + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run += psa + psb;
+        lq_run += qsa + qsb;
+
+        // -- rare: a term reached 2^32; find this tile's largest scores -----------
+        const bool ovf = !(psa < 4294967296.0f) || !(psb < 4294967296.0f);
+        if (__ballot(ovf) != 0ull) {
+          f32x16 ra = score_chain(sb, 0, [](int) {});
+          apply_mask(ra, 0);
+          m_hi = fmaxf(m_hi, half_row_max(ra));
+          f32x16 rb = score_chain(sb, 1, [](int) {});
+          apply_mask(rb, 1);
+          m_hi = fmaxf(m_hi, half_row_max(rb));
+          overflow = true;
         }
       }
       nv_cur = nv_next;
@@ -500,8 +536,7 @@ mla_split_kernel(MainArgs a) {
     const bool again = pass == 0 && *restart_flag != 0;
     __syncthreads();
     if (!again) break;
-    const float row_true = fmaxf(m_true, __shfl_xor(m_true, 32));
-    m_ref = row_true;
+    m_ref = fmaxf(m_ref, m_hi);
   }
 
   if (!wave_active) return;
@@ -580,22 +615,38 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   const int64_t rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
   const int64_t rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
 
+  // Every active split wrote its whole record (rows without keys as zeros with
+  // lse = -inf), so the loads below are unconditional and issued 8 at a time.
+  const float* lse_p = a.ws_lse + rec0 * kRowsPerWave + l32;
+  const float* o_p = a.ws_o + rec0 * kRecFloats + ((db * 4 + qq) * 64 + lane) * 4;
+  const int64_t lse_step = rec_stride * kRowsPerWave;
+  const int64_t o_step = rec_stride * kRecFloats;
   float mx = -__builtin_inff();
-  for (int s = 0; s < n_active; ++s)
-    mx = fmaxf(mx, a.ws_lse[(rec0 + s * rec_stride) * kRowsPerWave + l32]);
-
+  for (int s0 = 0; s0 < n_active; s0 += 8) {
+    float ls[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ls[j] = s0 + j < n_active ? lse_p[(s0 + j) * lse_step] : -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, ls[j]);
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (mx != -__builtin_inff()) {
-    for (int s = 0; s < n_active; ++s) {
-      const int64_t rec = rec0 + s * rec_stride;
-      const float ls = a.ws_lse[rec * kRowsPerWave + l32];
-      if (ls == -__builtin_inff()) continue;
-      const float w = fast_exp2(ls - mx);
-      wsum += w;
-      const f32x4 v =
-          *reinterpret_cast<const f32x4*>(a.ws_o + rec * kRecFloats + ((db * 4 + qq) * 64 + lane) * 4);
-      acc += w * v;
+    for (int s0 = 0; s0 < n_active; s0 += 8) {
+      float ls[8];
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool in = s0 + j < n_active;
+        ls[j] = in ? lse_p[(s0 + j) * lse_step] : -__builtin_inff();
+        v[j] = in ? *reinterpret_cast<const f32x4*>(o_p + (s0 + j) * o_step) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float w = ls[j] == -__builtin_inff() ? 0.f : fast_exp2(ls[j] - mx);
+        wsum += w;
+        acc += w * v[j];
+      }
     }
   }
   const bool live = wsum > 0.f;

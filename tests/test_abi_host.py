@@ -91,6 +91,9 @@ def call(lib, dims, sparse=False, ptrs=None, ws=None, ws_bytes=0, scale=0.1):
     dict(kw=dict(page_size=32, max_pages=5), ptrs=dict(pt=P())),  # not a multiple of 64
     dict(kw=dict(page_size=64, max_pages=2), ptrs=dict(pt=P())),  # 2*64 < max_kv_len
     dict(scale=float("nan")),
+    dict(scale=0.0),                        # the softmax scale must be positive
+    dict(scale=-0.1),
+    dict(scale=float("inf")),
 ])
 def test_invalid_arguments(lib, case):
     dims = None if "dims" in case else _dims(**case.get("kw", {}))
