@@ -101,6 +101,7 @@ int make_plan(const mla_dims* d, bool sparse, mla_plan_info* p) {
     if (splits < 1) splits = 1;
   }
   if (splits > tiles) splits = tiles;
+  if (splits > mlav::kMaxSplits) splits = mlav::kMaxSplits;
   int64_t chunk = ceil_div(tiles, splits);
   splits = ceil_div(tiles, chunk);
   const int64_t grid = row_blocks * splits * groups;
@@ -158,8 +159,8 @@ int run(const mla_dims* d, bool sparse, const uint16_t* q_lat, const uint16_t* q
   a.lse = lse;
   if (p.workspace_bytes > 0) {
     const size_t records = (size_t)p.num_splits * p.num_groups * p.row_blocks * kWaves;
-    a.ws_o = static_cast<float*>(workspace);
-    a.ws_lse = a.ws_o + records * mlav::kRecFloats;
+    a.ws_o = static_cast<uint16_t*>(workspace);
+    a.ws_lse = reinterpret_cast<float*>(a.ws_o + records * mlav::kRecElems);
   }
   a.kv_seq_stride = page_table ? 0 : d->kv_seq_stride;
   a.kv_rows = d->kv_rows;

@@ -15,9 +15,14 @@ constexpr int kRowsPerWave = 32;     // query rows owned by one wave (one per la
 constexpr int kRowsPerBlock = kWaves * kRowsPerWave;  // 128
 constexpr int kThreads = kWaves * 64;
 
-// Workspace record: one wave's 32 rows x 512 fp32 partial output, plus 32 lse values.
-constexpr int kRecFloats = kRowsPerWave * kDL;  // 16384
-constexpr size_t kRecBytes = (size_t)kRecFloats * 4 + (size_t)kRowsPerWave * 4;
+// Workspace record: one wave's 32 rows x 512 partial output (fp16, normalised by its
+// split's own sum of rounded terms, times a per-row power-of-two scale), plus three
+// fp32 values per row: the split's log2-sum-exp from fp32 terms, the same from the
+// rounded terms, and the row's fp16 scale.
+constexpr int kRecElems = kRowsPerWave * kDL;  // 16384
+constexpr int kRecRowStats = 3;
+constexpr int kMaxSplits = 256;  // per query group (combine weights live in LDS)
+constexpr size_t kRecBytes = (size_t)kRecElems * 2 + (size_t)kRecRowStats * kRowsPerWave * 4;
 
 enum Mode : int { kContig = 0, kPaged = 1, kSparse = 2, kSparsePaged = 3 };
 
@@ -32,8 +37,8 @@ struct MainArgs {
   const int32_t* indices;
   uint16_t* out;
   float* lse;
-  float* ws_o;    // [records][16384] fp32, register-native order
-  float* ws_lse;  // [records][32] fp32, log2 domain
+  uint16_t* ws_o; // [records][16384] fp16, register-native order
+  float* ws_lse;  // [records][3][32] fp32: lse2 (fp32 terms), lse2 (rounded terms), scale
   int64_t kv_seq_stride;
   int64_t kv_rows;
   int32_t T, H;

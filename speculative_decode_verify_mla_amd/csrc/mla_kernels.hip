@@ -223,9 +223,18 @@ mla_split_kernel(MainArgs a) {
   if (!kSparseMode && row_valid) {
     const int t = row / a.H;
     if (a.tree_mask != nullptr) {
+      // 16 independent byte loads per chunk, one wait per chunk
       const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.T + t) * a.T;
-      for (int j = 0; j < a.T; ++j)
-        if (mrow[j] != 0) vis |= 1ull << j;
+#pragma unroll
+      for (int j0 = 0; j0 < 64; j0 += 16) {
+        if (j0 < a.T) {
+          uint32_t m[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) m[j] = (j0 + j < a.T) ? mrow[j0 + j] : 0u;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) vis |= (uint64_t)(m[j] != 0u) << (j0 + j);
+        }
+      }
     } else {
       vis = (t >= 63) ? ~0ull : ((2ull << t) - 1ull);  // chain: drafts 0..t
     }
@@ -278,64 +287,82 @@ mla_split_kernel(MainArgs a) {
     return r < a.kv_rows ? (int)r : -1;
   };
 
-  // Dense: issue one tile; returns the number of leading keys that exist.
-  auto issue_dense = [&](int tile, int stage) -> int {
-    uint8_t* dst = smem + stage * kStageBytes;
+  // A tile's 18 loads of this wave (16 latent key rows, 2 x 8 rope rows),
+  // prepared once and issued one at a time: spread over the first score chain,
+  // they keep the vector-memory issue from stalling the wave.
+  struct TileLoad {
+    __amdgpu_buffer_rsrc_t rl, rr;
+    uint8_t* dst;
+    int rows;         // sparse: lane k holds key k's physical row (-1 = absent)
+    unsigned lane16;  // dense: 16 * lane, an opaque per-tile copy (see score_chain)
+  };
+  // Dense: returns the number of leading keys of the tile that exist in `nv`.
+  // A tile past the split (`tile` >= t_end) loads nothing: its loads read as
+  // out of range and only zero-fill the free stage.
+  auto prepare_dense = [&](int tile, int stage, int& nv) -> TileLoad {
     const int pos = tile * kTile;
-    int nv = min(kTile, kv_len - pos);
-    int64_t rbase;
-    if (kPagedMode) {
-      const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
-      rbase = (int64_t)page * a.page_size + pos % a.page_size;
-      if (page < 0 || rbase >= a.kv_rows) {
-        nv = 0;
-        rbase = 0;
-      } else if (rbase + nv > a.kv_rows) {
-        nv = (int)(a.kv_rows - rbase);
+    nv = tile < t_end ? min(kTile, kv_len - pos) : 0;
+    int64_t rbase = 0;
+    if (nv > 0) {
+      if (kPagedMode) {
+        const int page = a.page_table[(int64_t)b * a.max_pages + pos / a.page_size];
+        rbase = (int64_t)page * a.page_size + pos % a.page_size;
+        if (page < 0 || rbase >= a.kv_rows) {
+          nv = 0;
+          rbase = 0;
+        } else if (rbase + nv > a.kv_rows) {
+          nv = (int)(a.kv_rows - rbase);
+        }
+      } else {
+        rbase = seq_row0 + pos;
       }
     } else {
-      rbase = seq_row0 + pos;
+      nv = 0;
     }
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.c_kv + rbase * kDL, (uint32_t)nv * 1024u);
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.k_rope + rbase * kDR, (uint32_t)nv * 128u);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = wave + 4 * i;
-      buffer_to_lds(rl, dst + key * 1024, (unsigned)key * 1024u + lat_chunk_off(key));
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = wave + 4 * i;
-      buffer_to_lds(rr, dst + kLatBytes + j * 1024,
-                    (unsigned)j * 1024u + (unsigned)((lane >> 3) * 128) + rope_chunk_off);
-    }
-    return nv;
+    TileLoad tl;
+    tl.rl = make_rsrc(a.c_kv + rbase * kDL, (uint32_t)nv * 1024u);
+    tl.rr = make_rsrc(a.k_rope + rbase * kDR, (uint32_t)nv * 128u);
+    tl.dst = smem + stage * kStageBytes;
+    tl.rows = 0;
+    tl.lane16 = (unsigned)lane * 16u;
+    asm volatile("" : "+v"(tl.lane16));
+    return tl;
   };
-
-  // Sparse: issue one tile given lane k's physical row for key k.
-  // (the host limits sparse extents to 2^21 rows, so byte offsets stay below 2^31)
+  // Sparse: (the host limits sparse extents to 2^21 rows, so byte offsets stay below 2^31)
   const int64_t sparse_rows = kPagedMode ? a.kv_rows : (int64_t)kv_len;
-  auto issue_sparse = [&](int rows, int stage) {
-    uint8_t* dst = smem + stage * kStageBytes;
-    const __amdgpu_buffer_rsrc_t srl =
-        make_rsrc(a.c_kv + seq_row0 * kDL, (uint32_t)(sparse_rows * 1024));
-    const __amdgpu_buffer_rsrc_t srr =
-        make_rsrc(a.k_rope + seq_row0 * kDR, (uint32_t)(sparse_rows * 128));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
+  auto prepare_sparse = [&](int rows, int stage) -> TileLoad {
+    TileLoad tl;
+    tl.rl = make_rsrc(a.c_kv + seq_row0 * kDL, (uint32_t)(sparse_rows * 1024));
+    tl.rr = make_rsrc(a.k_rope + seq_row0 * kDR, (uint32_t)(sparse_rows * 128));
+    tl.dst = smem + stage * kStageBytes;
+    tl.rows = rows;
+    tl.lane16 = 0;
+    return tl;
+  };
+  auto load_one = [&](const TileLoad& tl, int i) {
+    if (i < 16) {
       const int key = wave + 4 * i;
-      const int r = __builtin_amdgcn_readlane(rows, key);
-      const unsigned off = r >= 0 ? (unsigned)r * 1024u + lat_chunk_off(key) : kOobOffset;
-      buffer_to_lds(srl, dst + key * 1024, off);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = wave + 4 * i;
-      const int r = __shfl(rows, 8 * j + (lane >> 3));
-      const unsigned off = r >= 0 ? (unsigned)r * 128u + rope_chunk_off : kOobOffset;
-      buffer_to_lds(srr, dst + kLatBytes + j * 1024, off);
+      unsigned off;
+      if (kSparseMode) {
+        const int r = __builtin_amdgcn_readlane(tl.rows, key);
+        off = r >= 0 ? (unsigned)r * 1024u + lat_chunk_off(key) : kOobOffset;
+      } else {
+        off = (tl.lane16 ^ (unsigned)(16 * swz_lat(key & 15))) + (unsigned)key * 1024u;
+      }
+      buffer_to_lds(tl.rl, tl.dst + key * 1024, off);
+    } else {
+      const int j = wave + 4 * (i - 16);
+      unsigned off;
+      if (kSparseMode) {
+        const int r = __shfl(tl.rows, 8 * j + (lane >> 3));
+        off = r >= 0 ? (unsigned)r * 128u + rope_chunk_off : kOobOffset;
+      } else {
+        off = (unsigned)j * 1024u + (unsigned)((lane >> 3) * 128) + rope_chunk_off;
+      }
+      buffer_to_lds(tl.rr, tl.dst + kLatBytes + j * 1024, off);
     }
   };
+  constexpr int kLoadsPerWave = 18;
 
   // ---- softmax state ------------------------------------------------------------
   // The accumulator is never rescaled inside the loop: every exponent is taken
@@ -435,13 +462,18 @@ mla_split_kernel(MainArgs a) {
     int nv_cur = 0, nv_next = 0;
     uint64_t vm_cur = 0, vm_next = 0;
     int idx_next = -1;
-    if (kSparseMode) {
-      const int r0 = resolve_row(fetch_index(t_begin));
-      vm_cur = __ballot(r0 >= 0);
-      issue_sparse(r0, 0);
-      if (t_begin + 1 < t_end) idx_next = fetch_index(t_begin + 1);
-    } else {
-      nv_cur = issue_dense(t_begin, 0);
+    {
+      TileLoad tl0;
+      if (kSparseMode) {
+        const int r0 = resolve_row(fetch_index(t_begin));
+        vm_cur = __ballot(r0 >= 0);
+        tl0 = prepare_sparse(r0, 0);
+        if (t_begin + 1 < t_end) idx_next = fetch_index(t_begin + 1);
+      } else {
+        tl0 = prepare_dense(t_begin, 0, nv_cur);
+      }
+#pragma unroll
+      for (int i = 0; i < kLoadsPerWave; ++i) load_one(tl0, i);
     }
     if (threadIdx.x == 0) *restart_flag = 0;
 
@@ -449,15 +481,19 @@ mla_split_kernel(MainArgs a) {
       const int stage = (tile - t_begin) & 1;
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads (tile data, prefetched indices) landed
       __syncthreads();                // ... and every other wave's; previous stage is free
-      if (tile + 1 < t_end) {
-        if (kSparseMode) {
-          const int r1 = resolve_row(idx_next);
-          vm_next = __ballot(r1 >= 0);
-          issue_sparse(r1, stage ^ 1);
-          if (tile + 2 < t_end) idx_next = fetch_index(tile + 2);
-        } else {
-          nv_next = issue_dense(tile + 1, stage ^ 1);
-        }
+      // The next tile's loads (past the split's end: none that touch memory).
+      TileLoad nl;
+      if (kSparseMode) {
+        const int r1 = tile + 1 < t_end ? resolve_row(idx_next) : -1;
+        vm_next = __ballot(r1 >= 0);
+        nl = prepare_sparse(r1, stage ^ 1);
+        if (tile + 2 < t_end) idx_next = fetch_index(tile + 2);
+      } else {
+        nl = prepare_dense(tile + 1, stage ^ 1, nv_next);
+      }
+      if (!wave_active) {
+#pragma unroll
+        for (int i = 0; i < kLoadsPerWave; ++i) load_one(nl, i);
       }
 
       if (wave_active) {
@@ -478,7 +514,10 @@ mla_split_kernel(MainArgs a) {
         bf16x8 pk[4];
 
         // -- S_a: scores of keys 0..31 ----------------------------------------------
-        f32x16 sa = score_chain(sb, 0, [](int) {});
+        // the next tile's loads go out between these MFMAs, one every second step
+        f32x16 sa = score_chain(sb, 0, [&](int c) {
+          if ((c & 1) == 0 && (c >> 1) < kLoadsPerWave) load_one(nl, c >> 1);
+        });
         apply_mask(sa, 0);
         init_reference(sa);
         const float mu_a = m_ref == -__builtin_inff() ? 0.f : m_ref;
@@ -568,96 +607,147 @@ mla_split_kernel(MainArgs a) {
   } else {
     const int64_t rec =
         (((int64_t)split * a.num_groups + group) * a.row_blocks + rb) * kWaves + wave;
-    float* dst = a.ws_o + rec * kRecFloats;
+    // fp16 with a per-row power-of-two scale keeps 11 significant bits of the
+    // normalised partial (|o| <= the largest value-row entry) at half the bytes.
+    float amax = 0.f;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[db][r]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32)) * inv;
+    // scale = 2^(e-15) with amax < 2^e, so |o / scale| < 2^15 fits fp16
+    const float scale = amax > 0.f ? __builtin_ldexpf(1.0f, __builtin_amdgcn_frexp_expf(amax) - 15) : 1.0f;
+    const float inv_s = inv / scale;
+    uint16_t* dst = a.ws_o + rec * kRecElems;
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        f32x4 v = {o[db][4 * qq + 0] * inv, o[db][4 * qq + 1] * inv, o[db][4 * qq + 2] * inv,
-                   o[db][4 * qq + 3] * inv};
-        *reinterpret_cast<f32x4*>(dst + ((db * 4 + qq) * 64 + lane) * 4) = v;
+        const _Float16 h0 = (_Float16)(o[db][4 * qq + 0] * inv_s), h1 = (_Float16)(o[db][4 * qq + 1] * inv_s);
+        const _Float16 h2 = (_Float16)(o[db][4 * qq + 2] * inv_s), h3 = (_Float16)(o[db][4 * qq + 3] * inv_s);
+        uint2 pkd;
+        pkd.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        pkd.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+        *reinterpret_cast<uint2*>(dst + ((db * 4 + qq) * 64 + lane) * 4) = pkd;
       }
     }
-    if (half == 0) a.ws_lse[rec * kRowsPerWave + l32] = lse2;
+    if (half == 0) {
+      float* st = a.ws_lse + rec * (kRecRowStats * kRowsPerWave) + l32;
+      st[0] = lse2;
+      st[kRowsPerWave] = live && lq_row > 0.f ? m_ref + fast_log2(lq_row) : -__builtin_inff();
+      st[2 * kRowsPerWave] = scale;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel: lse = log2 sum_s 2^{lse_s}; out = sum_s 2^{lse_s - lse} o_s.
-// One thread per 4 consecutive output dims of one row. A wave record (32 rows
-// x 512 dims = 4096 float4) is covered by 16 blocks of 256 threads.
+// Combine kernel: lse = log2 sum_s 2^{lse_s}; out = sum_s w_s o_s with
+// w_s = 2^{lq_s} / sum_s' 2^{lq_s'}, where lq_s is split s's log2-sum of the
+// rounded terms its partial was normalised by (an exact convex combination of
+// the accumulated terms) and lse_s the same from fp32 terms.
+// Block = one 32-dim block of one wave record (32 rows x 32 dims). The block
+// first turns the (row, split) statistics into normalised weights in LDS, then
+// each thread issues all its split loads before accumulating.
 // ---------------------------------------------------------------------------
-static_assert(16 * 256 * 4 == kRecFloats, "16 combine blocks of 256 float4 cover one wave record");
+static_assert(16 * 256 * 4 == kRecElems, "16 combine blocks of 256 threads x 4 dims cover one wave record");
 
 template <int MODE>
 __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
+  __shared__ float wts[kRowsPerWave][kMaxSplits + 1];  // normalised weight x fp16 scale
+  __shared__ float red[3][8][kRowsPerWave];
+  __shared__ float row_lse[kRowsPerWave];
+
   const int bid = blockIdx.x;
-  const int part = bid & 15;
+  const int db = bid & 15;
   const int wrec = bid >> 4;
   const int wave = wrec & 3;
   const int rbg = wrec >> 2;
   const int rb = rbg % a.row_blocks;
   const int group = rbg / a.row_blocks;
-
-  const int idx = part * 256 + threadIdx.x;  // 0..4095
-  const int lane = idx & 63;
-  const int qq = (idx >> 6) & 3;
-  const int db = idx >> 8;                    // 0..15
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-  const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
-  if (row >= a.rows_per_group) return;
-  const int64_t qrow = (int64_t)group * a.rows_per_group + row;
+  const int t = threadIdx.x;
+  if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;  // padding wave record
 
   const GroupInfo gi = group_info(a, group, kSparseMode);
   const int n_active = min(a.num_splits, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
   const int64_t rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
   const int64_t rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
+  const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
 
-  // Every active split wrote its whole record (rows without keys as zeros with
-  // lse = -inf), so the loads below are unconditional and issued 8 at a time.
-  const float* lse_p = a.ws_lse + rec0 * kRowsPerWave + l32;
-  const float* o_p = a.ws_o + rec0 * kRecFloats + ((db * 4 + qq) * 64 + lane) * 4;
-  const int64_t lse_step = rec_stride * kRowsPerWave;
-  const int64_t o_step = rec_stride * kRecFloats;
-  float mx = -__builtin_inff();
-  for (int s0 = 0; s0 < n_active; s0 += 8) {
-    float ls[8];
+  // ---- phase 1: per-row maxima, sums and weights (thread = row x split lane) ----
+  {
+    const int r = t & 31, sl = t >> 5;  // 8 split lanes per row
+    const float* st = a.ws_lse + rec0 * (kRecRowStats * kRowsPerWave) + r;
+    float mx = -__builtin_inff(), mxq = -__builtin_inff();
+    for (int s = sl; s < n_active; s += 8) {
+      mx = fmaxf(mx, st[s * st_step]);
+      mxq = fmaxf(mxq, st[s * st_step + kRowsPerWave]);
+    }
+    red[0][sl][r] = mx;
+    red[1][sl][r] = mxq;
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ls[j] = s0 + j < n_active ? lse_p[(s0 + j) * lse_step] : -__builtin_inff();
+    for (int j = 0; j < 8; ++j) {
+      mx = fmaxf(mx, red[0][j][r]);
+      mxq = fmaxf(mxq, red[1][j][r]);
+    }
+    __syncthreads();
+    float es = 0.f, ws = 0.f;
+    for (int s = sl; s < n_active; s += 8) {
+      const float le = st[s * st_step], lq = st[s * st_step + kRowsPerWave];
+      const float w = lq == -__builtin_inff() ? 0.f : fast_exp2(lq - mxq);
+      es += le == -__builtin_inff() ? 0.f : fast_exp2(le - mx);
+      ws += w;
+      wts[r][s] = w * st[s * st_step + 2 * kRowsPerWave];
+    }
+    red[0][sl][r] = es;
+    red[1][sl][r] = ws;
+    __syncthreads();
+    es = 0.f;
+    ws = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, ls[j]);
+    for (int j = 0; j < 8; ++j) {
+      es += red[0][j][r];
+      ws += red[1][j][r];
+    }
+    const float inv = ws > 0.f ? 1.0f / ws : 0.f;
+    for (int s = sl; s < n_active; s += 8) wts[r][s] *= inv;
+    if (sl == 0)
+      row_lse[r] = (mx != -__builtin_inff() && es > 0.f) ? (mx + fast_log2(es)) * kLn2 : -__builtin_inff();
+    __syncthreads();
   }
+
+  // ---- phase 2: out = sum_s w_s o_s for 4 dims per thread -------------------------
+  const int lane = t & 63, qq = t >> 6, half = lane >> 5, l32 = lane & 31;
+  const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
+  const uint16_t* o_p = a.ws_o + rec0 * kRecElems + ((db * 4 + qq) * 64 + lane) * 4;
+  const int64_t o_step = rec_stride * kRecElems;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (mx != -__builtin_inff()) {
-    for (int s0 = 0; s0 < n_active; s0 += 8) {
-      float ls[8];
-      f32x4 v[8];
+  for (int s0 = 0; s0 < n_active; s0 += 16) {
+    uint2 raw[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool in = s0 + j < n_active;
-        ls[j] = in ? lse_p[(s0 + j) * lse_step] : -__builtin_inff();
-        v[j] = in ? *reinterpret_cast<const f32x4*>(o_p + (s0 + j) * o_step) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int j = 0; j < 16; ++j)
+      raw[j] = s0 + j < n_active ? *reinterpret_cast<const uint2*>(o_p + (s0 + j) * o_step) : uint2{0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float w = ls[j] == -__builtin_inff() ? 0.f : fast_exp2(ls[j] - mx);
-        wsum += w;
-        acc += w * v[j];
+    for (int j = 0; j < 16; ++j) {
+      if (s0 + j < n_active) {
+        const float w = wts[l32][s0 + j];
+        acc[0] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].x & 0xffffu));
+        acc[1] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].x >> 16));
+        acc[2] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].y & 0xffffu));
+        acc[3] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].y >> 16));
       }
     }
   }
-  const bool live = wsum > 0.f;
-  const float inv = live ? 1.0f / wsum : 0.f;
+  if (row >= a.rows_per_group) return;
+  const int64_t qrow = (int64_t)group * a.rows_per_group + row;
   const int d = db * 32 + 8 * qq + 4 * half;
   uint2 pkd;
-  pkd.x = (uint32_t)bf16_bits(acc[0] * inv) | ((uint32_t)bf16_bits(acc[1] * inv) << 16);
-  pkd.y = (uint32_t)bf16_bits(acc[2] * inv) | ((uint32_t)bf16_bits(acc[3] * inv) << 16);
+  pkd.x = (uint32_t)bf16_bits(acc[0]) | ((uint32_t)bf16_bits(acc[1]) << 16);
+  pkd.y = (uint32_t)bf16_bits(acc[2]) | ((uint32_t)bf16_bits(acc[3]) << 16);
   *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
-  if (db == 0 && qq == 0 && half == 0)
-    a.lse[qrow] = live ? (mx + fast_log2(wsum)) * kLn2 : -__builtin_inff();
+  if (db == 0 && qq == 0 && half == 0) a.lse[qrow] = row_lse[l32];
 }
 
 // ---------------------------------------------------------------------------

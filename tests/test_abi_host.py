@@ -132,7 +132,7 @@ def test_plan_shapes():
     p = mv.plan(d)
     assert (p.row_blocks, p.num_groups, p.rows_per_group) == (8, 1, 1024)
     assert p.num_splits * p.chunk_tiles >= 1025 > (p.num_splits - 1) * p.chunk_tiles
-    assert p.workspace_bytes == p.num_splits * 8 * 4 * (32 * 512 * 4 + 32 * 4)
+    assert p.workspace_bytes == p.num_splits * 8 * 4 * (32 * 512 * 2 + 3 * 32 * 4)
     # tiny chain: one split, no workspace
     p1 = mv.plan(_dims())
     assert p1.num_splits == 1 and p1.workspace_bytes == 0
