@@ -69,12 +69,16 @@ constexpr int kFragAhead = MLA_FRAG_AHEAD;
 
 // ---------------------------------------------------------------------------
 // LDS swizzles. A tile is stored row-major (key-major) with its 16-byte chunks
-// permuted inside each key row so that the two read patterns are free of bank
-// conflicts: 16 consecutive keys reading the same logical chunk (S^T operand),
-// and 4 consecutive keys x 32 bytes (transposing V^T read).
+// permuted inside each key row so that both read patterns are free of bank
+// conflicts on the 64 four-byte LDS banks:
+//  - S^T operand (16-byte reads, 16 lanes per bank pass): 16 consecutive keys
+//    read the same logical chunk, so swz_lat must be a bijection on key mod 16;
+//  - V^T operand (transposing 8-byte reads, 32 lanes per bank pass): 4
+//    consecutive keys read the same 4 aligned logical chunks, so swz_lat must
+//    give the 4 keys of an aligned quad distinct values in bits 2..3.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz_lat(int key) {  // permutes the low 4 chunk bits
-  return ((key & 3) << 1) | ((key >> 2) & 1) | (key & 8);
+  return ((key & 3) << 2) | ((key >> 2) & 3);
 }
 __device__ __forceinline__ int swz_rope(int key) {  // permutes the 3 chunk bits
   return ((key >> 1) ^ (key << 2)) & 7;
@@ -513,40 +517,65 @@ mla_split_kernel(MainArgs a) {
         float psa = 0.f, qsa = 0.f, psb = 0.f, qsb = 0.f;
         bf16x8 pk[4];
 
-        // -- S_a: scores of keys 0..31 ----------------------------------------------
-        // the next tile's loads go out between these MFMAs, one every second step
-        f32x16 sa = score_chain(sb, 0, [&](int c) {
-          if ((c & 1) == 0 && (c >> 1) < kLoadsPerWave) load_one(nl, c >> 1);
-        });
-        apply_mask(sa, 0);
-        init_reference(sa);
-        const float mu_a = m_ref == -__builtin_inff() ? 0.f : m_ref;
-
-        // -- S_b on the matrix cores while the VALU exponentiates S_a ---------------
-        f32x16 sbk = score_chain(sb, 1, [&](int c) { softmax_step(c, sa, mu_a, psa, qsa, pk); });
-        apply_mask(sbk, 1);
-        init_reference(sbk);
-        const float mu_b = m_ref == -__builtin_inff() ? 0.f : m_ref;
-
-        // -- O^T += V^T P^T over keys 0..31 while the VALU exponentiates S_b; then
-        //    keys 32..63. Step = (16-key chunk kc) x (32-dim block db); V^T
-        //    fragments are read one step ahead. -----------------------------------
-        unsigned vb0 = vbase[0], vb1 = vbase[1];
-        asm volatile("" : "+v"(vb0), "+v"(vb1));  // see score_chain
-        auto v_frag = [&](int step) -> bf16x8 {
-          const int kc = step >> 4, db = step & 15;
+        // One stream of 136 LDS operand fragments per tile: 36 K fragments of
+        // keys 0..31 (S_a), 36 of keys 32..63 (S_b), then 64 V^T fragments (PV,
+        // step = 16-key chunk kc x 32-dim block db). Each is read kFragAhead
+        // steps before its MFMA, across the chain boundaries too, so no chain
+        // starts on an LDS round trip. The VALU work is written between the
+        // MFMAs: the next tile's loads in S_a, S_a's softmax in S_b, S_b's in PV.
+        unsigned kbase = kbaseA, vb0 = vbase[0], vb1 = vbase[1];
+        asm volatile("" : "+v"(kbase), "+v"(vb0), "+v"(vb1));  // see score_chain
+        auto frag = [&](int f) -> bf16x8 {
+          if (f < 72) {
+            const int kb = f / 36, c = f % 36;
+            const unsigned off =
+                c < 32 ? (kbase ^ (unsigned)(32 * (c & 7))) + (unsigned)((c >> 3) * 256 + kb * 32 * 1024)
+                       : (unsigned)(kLatBytes + (l32 + 32 * kb) * 128 + (((2 * (c - 32)) ^ yrope) * 16));
+            return lds_read16(sb, off);
+          }
+          const int step = f - 72, kc = step >> 4, db = step & 15;
           const unsigned hi = (unsigned)((db >> 2) * 256 + kc * 16384);
           const bf16x4 v0 = lds_read_tr(sb, (vb0 ^ (unsigned)(64 * (db & 3))) + hi);
           const bf16x4 v1 = lds_read_tr(sb, (vb1 ^ (unsigned)(64 * (db & 3))) + hi);
           return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         };
-        bf16x8 vf[kFragAhead];
+        bf16x8 ring[kFragAhead];
 #pragma unroll
-        for (int j = 0; j < kFragAhead; ++j) vf[j] = v_frag(j);
+        for (int j = 0; j < kFragAhead; ++j) ring[j] = frag(j);
+        // S_a: scores of keys 0..31
+        f32x16 sa;
 #pragma unroll
-        for (int step = 0; step < 64; ++step) {
-          o[step & 15] = mfma32(vf[step % kFragAhead], pk[step >> 4], o[step & 15]);
-          if (step + kFragAhead < 64) vf[step % kFragAhead] = v_frag(step + kFragAhead);
+        for (int f = 0; f < 36; ++f) {
+          if (f == 0) sa = mfma32_v_first(ring[0], q[0]);
+          else mfma32_v_acc(sa, ring[f % kFragAhead], q[f]);
+          ring[f % kFragAhead] = frag(f + kFragAhead);
+          if ((f & 1) == 0 && (f >> 1) < kLoadsPerWave) load_one(nl, f >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        score_fence(sa);
+        apply_mask(sa, 0);
+        init_reference(sa);
+        const float mu_a = m_ref == -__builtin_inff() ? 0.f : m_ref;
+        // S_b: scores of keys 32..63, S_a's softmax on the VALU
+        f32x16 sbk;
+#pragma unroll
+        for (int f = 36; f < 72; ++f) {
+          if (f == 36) sbk = mfma32_v_first(ring[f % kFragAhead], q[0]);
+          else mfma32_v_acc(sbk, ring[f % kFragAhead], q[f - 36]);
+          ring[f % kFragAhead] = frag(f + kFragAhead);
+          softmax_step(f - 36, sa, mu_a, psa, qsa, pk);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        score_fence(sbk);
+        apply_mask(sbk, 1);
+        init_reference(sbk);
+        const float mu_b = m_ref == -__builtin_inff() ? 0.f : m_ref;
+        // PV: O^T += V^T P^T, S_b's softmax on the VALU
+#pragma unroll
+        for (int f = 72; f < 136; ++f) {
+          const int step = f - 72;
+          o[step & 15] = mfma32(ring[f % kFragAhead], pk[step >> 4], o[step & 15]);
+          if (f + kFragAhead < 136) ring[f % kFragAhead] = frag(f + kFragAhead);
           if (step < 32) softmax_step(step, sbk, mu_b, psb, qsb, pk + 2);
           __builtin_amdgcn_sched_barrier(0);
         }
