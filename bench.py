@@ -110,8 +110,8 @@ def cpu_baseline(w, budget_s: float):
     el = time.perf_counter() - t0
     per_call_us = el / done * len(tokens) * 1e6
     return dict(value=per_call_us, unit="us/call", cores=int(threads), kind="oracle",
-                sample=f"{done} of the call's {len(tokens)} (sequence, draft-token) groups, "
-                       f"all {w.H} heads each, fp64 numpy oracle, {el:.1f} s wall; "
+                sample=f"{done} (sequence, draft-token) groups of {w.H} heads each, cycling "
+                       f"through the call's {len(tokens)}, fp64 numpy oracle, {el:.1f} s wall; "
                        f"scaled to one whole call")
 
 

@@ -107,7 +107,9 @@ typedef struct mla_dims {
   int64_t kv_seq_stride; /* contiguous: rows between consecutive sequences */
   int64_t kv_rows;       /* rows of the c_kv and k_rope allocations */
   int32_t topk;          /* sparse: index-list length per token (ignored by the dense call) */
-  int32_t num_splits;    /* 0 = automatic; else requested KV splits per query group */
+  int32_t num_splits;    /* 0 = automatic; else requested KV splits per query group. The
+                            plan caps it at the tile count and at 256, then evens the
+                            tiles per split (the plan reports the splits used). */
   int32_t phase;         /* MLA_PHASE_* */
   int32_t reserved;      /* must be 0 */
 } mla_dims;
