@@ -115,13 +115,14 @@ typedef struct mla_dims {
 } mla_dims;
 
 typedef struct mla_plan_info {
-  int32_t num_splits;     /* KV splits per query group actually used */
-  int32_t chunk_tiles;    /* 64-key tiles per split */
+  int32_t num_splits;     /* KV splits per query group (dense: for a group of max_kv_len keys) */
+  int32_t chunk_tiles;    /* 64-key tiles per split (dense: for a group of max_kv_len keys) */
   int32_t row_blocks;     /* 128-row blocks per query group */
   int32_t num_groups;     /* query groups: B (dense) or B*T (sparse) */
   int32_t rows_per_group; /* T*H (dense) or H (sparse) */
-  int32_t reserved;
-  size_t workspace_bytes; /* device bytes the call needs; 0 when num_splits == 1 */
+  int32_t split_slots;    /* (group, split) slots per row block; the workspace holds
+                             split_slots * row_blocks * 4 records */
+  size_t workspace_bytes; /* device bytes the call needs; 0 when there is one slot in all */
 } mla_plan_info;
 
 /* Work decomposition of a call with these dims (sparse != 0: mla_sparse_attn).
@@ -136,7 +137,7 @@ size_t mla_verify_workspace_bytes(const mla_dims* dims, int sparse);
  * Checks (MLA_ERR_INVALID): dims, q_lat, q_rope, c_kv, k_rope, kv_lens, out,
  * lse non-NULL; bf16 arrays 16-byte aligned, lse/kv_lens/page_table 4-byte
  * aligned; scale finite and > 0; B >= 1, 1 <= T <= 64, H >= 1;
- * T <= max_kv_len; num_splits >= 0;
+ * T <= max_kv_len; B * ceil(max_kv_len / 64) < 2^31; num_splits >= 0;
  * phase valid; reserved == 0; contiguous: page_table NULL, page_size 0,
  * kv_seq_stride >= max_kv_len and (B-1)*kv_seq_stride + max_kv_len <= kv_rows;
  * paged: page_table non-NULL, page_size a positive multiple of 64,

@@ -58,7 +58,7 @@ class MlaPlanInfo(ctypes.Structure):
         ("row_blocks", ctypes.c_int32),
         ("num_groups", ctypes.c_int32),
         ("rows_per_group", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("split_slots", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

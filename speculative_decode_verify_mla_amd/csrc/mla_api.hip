@@ -4,6 +4,7 @@
 // allocates, frees, synchronises or reads device memory on the host.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -36,6 +37,8 @@ int check_dims(const mla_dims* d, bool sparse, bool paged) {
   if (d->max_kv_len < 1 || d->kv_rows < 1) return MLA_ERR_INVALID;
   if (!sparse && d->max_kv_len < d->num_q) return MLA_ERR_INVALID;
   if (sparse && d->topk < 1) return MLA_ERR_INVALID;
+  // the dense split plan sums 64-key tiles over the batch in 32-bit integers
+  if (!sparse && (int64_t)d->batch * ceil_div(d->max_kv_len, kTile) > 0x7fffffffLL) return MLA_ERR_INVALID;
   // row counts must fit 32-bit grid arithmetic
   const int64_t rows_total = (int64_t)d->batch * d->num_q * d->num_heads;
   if (rows_total > (int64_t)1 << 30) return MLA_ERR_INVALID;
@@ -87,33 +90,52 @@ int make_plan(const mla_dims* d, bool sparse, mla_plan_info* p) {
   const int64_t row_blocks = ceil_div(rows, kRowsPerBlock);
   const int64_t keys = sparse ? d->topk : d->max_kv_len;
   const int64_t tiles = ceil_div(keys, kTile);
-  int64_t splits;
-  if (d->num_splits > 0) {
-    splits = d->num_splits;
+  // One workgroup per CU (LDS-bound). Splits keep a minimum of tiles each
+  // (mlav::kMinChunkSparse / kMinChunkDense) so the per-split partial (1 KiB per
+  // row) stays small next to the split's KV reads and matrix work.
+  const int64_t min_chunk = sparse ? mlav::kMinChunkSparse : mlav::kMinChunkDense;
+  const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(tiles / min_chunk, mlav::kMaxSplits));
+  int64_t splits, chunk, slots;
+  int64_t fixed_chunk = 0;
+  if (sparse) {
+    // Every token has the same number of index tiles: uniform splits.
+    splits = d->num_splits > 0 ? d->num_splits
+                               : std::max<int64_t>(1, std::min(device_cus() / (groups * row_blocks), cap));
+    splits = std::min<int64_t>(std::min<int64_t>(splits, tiles), mlav::kMaxSplits);
+    chunk = ceil_div(tiles, splits);
+    splits = ceil_div(tiles, chunk);
+    slots = splits * groups;
   } else {
-    // One workgroup per CU (LDS-bound): spread the keys of each query group
-    // over enough splits to cover the CUs once, but keep >= 4 tiles per split
-    // so the per-split partial (2 KB per row) stays small next to its KV reads.
-    const int64_t per_split = groups * row_blocks;
-    splits = device_cus() / per_split;
-    const int64_t min_tiles_cap = tiles / 4;
-    if (splits > min_tiles_cap) splits = min_tiles_cap;
-    if (splits < 1) splits = 1;
+    // Dense: the host fixes the (sequence, split) slots per row block; the
+    // kernels share them out by the sequences' actual lengths (kv_lens lives on
+    // the device). A requested split count fixes the chunk instead.
+    if (d->num_splits > 0) {
+      const int64_t req = std::min<int64_t>(std::min<int64_t>(d->num_splits, tiles), mlav::kMaxSplits);
+      fixed_chunk = ceil_div(tiles, req);
+      splits = ceil_div(tiles, fixed_chunk);
+      slots = groups * splits;
+    } else {
+      slots = std::max<int64_t>(groups, std::min(device_cus() / row_blocks, groups * cap));
+      splits = std::max<int64_t>(1, slots / groups);  // as if every sequence had max_kv_len keys
+    }
+    chunk = ceil_div(tiles, splits);
+    splits = ceil_div(tiles, chunk);
+    if (groups == 1) slots = splits;  // one sequence: exactly its evened splits
   }
-  if (splits > tiles) splits = tiles;
-  if (splits > mlav::kMaxSplits) splits = mlav::kMaxSplits;
-  int64_t chunk = ceil_div(tiles, splits);
-  splits = ceil_div(tiles, chunk);
-  const int64_t grid = row_blocks * splits * groups;
-  if (grid > 0x7fffffff) return MLA_ERR_INVALID;
+  const int64_t slot_stride = slots;
+  const int64_t grid = sparse ? row_blocks * slots : row_blocks * slot_stride;
+  if (grid > 0x7fffffff || slots > 0x7fffffff) return MLA_ERR_INVALID;
   p->num_splits = (int32_t)splits;
-  p->chunk_tiles = (int32_t)chunk;
+  p->chunk_tiles = (int32_t)(fixed_chunk > 0 ? fixed_chunk : chunk);
   p->row_blocks = (int32_t)row_blocks;
   p->num_groups = (int32_t)groups;
   p->rows_per_group = (int32_t)rows;
-  p->reserved = 0;
-  p->workspace_bytes =
-      splits > 1 ? (size_t)splits * groups * row_blocks * kWaves * mlav::kRecBytes : 0;
+  p->split_slots = (int32_t)slots;
+  // One slot in all: the split kernel writes out/lse directly, no workspace.
+  const bool single = sparse ? splits == 1 : slots == 1;
+  // records, then (dense, several sequences) the per-sequence record map
+  const size_t meta = (!sparse && groups > 1) ? (size_t)groups * sizeof(int2) : 0;
+  p->workspace_bytes = single ? 0 : (size_t)slots * row_blocks * kWaves * mlav::kRecBytes + meta;
   return MLA_OK;
 }
 
@@ -158,9 +180,11 @@ int run(const mla_dims* d, bool sparse, const uint16_t* q_lat, const uint16_t* q
   a.out = out;
   a.lse = lse;
   if (p.workspace_bytes > 0) {
-    const size_t records = (size_t)p.num_splits * p.num_groups * p.row_blocks * kWaves;
+    const size_t records = (size_t)p.split_slots * p.row_blocks * kWaves;
     a.ws_o = static_cast<uint16_t*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(a.ws_o + records * mlav::kRecElems);
+    if (!sparse && p.num_groups > 1)
+      a.ws_meta = reinterpret_cast<int2*>(a.ws_lse + records * mlav::kRecRowStats * mlav::kRowsPerWave);
   }
   a.kv_seq_stride = page_table ? 0 : d->kv_seq_stride;
   a.kv_rows = d->kv_rows;
@@ -175,7 +199,10 @@ int run(const mla_dims* d, bool sparse, const uint16_t* q_lat, const uint16_t* q
   a.topk = sparse ? d->topk : 0;
   a.num_splits = p.num_splits;
   a.chunk_tiles = p.chunk_tiles;
-  a.final_out = p.num_splits == 1 ? 1 : 0;
+  a.split_slots = p.split_slots;
+  a.slot_stride = p.split_slots;
+  a.fixed_chunk = (!sparse && d->num_splits > 0) ? p.chunk_tiles : 0;
+  a.final_out = p.workspace_bytes == 0 ? 1 : 0;
   a.scale_log2 = scale * 1.4426950408889634f;
 
   const int mode = sparse ? (page_table ? mlav::kSparsePaged : mlav::kSparse)

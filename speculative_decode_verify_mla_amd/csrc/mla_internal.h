@@ -22,6 +22,11 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kRecElems = kRowsPerWave * kDL;  // 16384
 constexpr int kRecRowStats = 3;
 constexpr int kMaxSplits = 256;  // per query group (combine weights live in LDS)
+// Fewest 64-key tiles per split when the library picks the split count: the
+// per-split partial (1 KiB per row, written and read back) and the split's fixed
+// start-up stay small next to its KV reads and matrix work.
+constexpr int kMinChunkDense = 4;
+constexpr int kMinChunkSparse = 4;
 constexpr size_t kRecBytes = (size_t)kRecElems * 2 + (size_t)kRecRowStats * kRowsPerWave * 4;
 
 enum Mode : int { kContig = 0, kPaged = 1, kSparse = 2, kSparsePaged = 3 };
@@ -39,6 +44,7 @@ struct MainArgs {
   float* lse;
   uint16_t* ws_o; // [records][16384] fp16, register-native order
   float* ws_lse;  // [records][3][32] fp32: lse2 (fp32 terms), lse2 (rounded terms), scale
+  int2* ws_meta;  // dense: [groups] (first slot, splits holding keys), written by the split kernel
   int64_t kv_seq_stride;
   int64_t kv_rows;
   int32_t T, H;
@@ -49,9 +55,12 @@ struct MainArgs {
   int32_t max_pages;
   int32_t max_kv_len;
   int32_t topk;
-  int32_t num_splits;
-  int32_t chunk_tiles;
-  int32_t final_out;   // 1: single split, write out/lse directly
+  int32_t num_splits;   // sparse: splits per token (uniform)
+  int32_t chunk_tiles;  // sparse: tiles per split
+  int32_t split_slots;  // dense: (sequence, split) slots per row block
+  int32_t slot_stride;  // dense: workgroups per row block in the grid (= split_slots)
+  int32_t fixed_chunk;  // dense: tiles per split when requested, 0 = chosen on the device
+  int32_t final_out;    // 1: single split for every group, write out/lse directly
   float scale_log2;    // scale * log2(e)
 };
 

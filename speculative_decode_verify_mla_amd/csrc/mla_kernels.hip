@@ -150,15 +150,136 @@ struct GroupInfo {
   int n_tiles;  // 64-key tiles covering the group's key list
 };
 
+__device__ __forceinline__ int clamped_kv_len(const MainArgs& a, int b) {
+  const int kv = a.kv_lens[b];
+  return kv < 0 ? 0 : (kv > a.max_kv_len ? a.max_kv_len : kv);
+}
+
 __device__ __forceinline__ GroupInfo group_info(const MainArgs& a, int group, bool sparse) {
   GroupInfo g;
   g.b = sparse ? group / a.T : group;
-  int kv = a.kv_lens[g.b];
-  kv = kv < 0 ? 0 : (kv > a.max_kv_len ? a.max_kv_len : kv);
-  g.kv_len = kv;
-  const int n_keys = sparse ? a.topk : kv;
+  g.kv_len = clamped_kv_len(a, g.b);
+  const int n_keys = sparse ? a.topk : g.kv_len;
   g.n_tiles = (n_keys + kTile - 1) / kTile;
   return g;
+}
+
+// ---------------------------------------------------------------------------
+// Dense split plan, computed on the device from kv_lens (the host only fixes
+// the number of (sequence, split) slots, a.split_slots = P, per row block).
+// Every sequence b with t_b tiles gets n_b = max(1, ceil(t_b / C)) consecutive
+// slots, where the chunk C is the smallest value >= max(kMinChunkDense, ceil(sum t / P),
+// ceil(max t / kMaxSplits)) with sum_b n_b <= P, so a ragged batch spreads its
+// tiles evenly over the slots instead of planning every sequence for the
+// longest one. Within a sequence the tiles are then spread evenly over its
+// slots. Pure integer arithmetic over kv_lens, evaluated identically by every
+// wave of both kernels (all lanes of a wave take part; results are uniform).
+// ---------------------------------------------------------------------------
+// Wave reductions. The result is the same in every lane; readfirstlane tells
+// the compiler so, which keeps everything derived from it (split bounds, tile
+// loop counters) in scalar registers and the tile loop free of divergence.
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int seq_slots(int t, int chunk) { return t > 0 ? (t + chunk - 1) / chunk : 1; }
+__device__ __forceinline__ int seq_tiles(const MainArgs& a, int b) {
+  return (clamped_kv_len(a, b) + kTile - 1) / kTile;
+}
+
+// Tiles of sequence `lane` (lane < num_groups <= 64), or of lane-strided
+// sequences when the batch is larger; one read of kv_lens per wave.
+struct BatchTiles {
+  int t;      // tiles of sequence i0 + lane for the first block (i0 = 0)
+  bool small; // num_groups <= 64: t covers the whole batch
+};
+__device__ __forceinline__ BatchTiles batch_tiles(const MainArgs& a) {
+  const int lane = threadIdx.x & 63;
+  BatchTiles bt;
+  bt.small = a.num_groups <= 64;
+  bt.t = lane < a.num_groups ? seq_tiles(a, lane) : 0;
+  return bt;
+}
+// sum over the batch of f(t_b) (f returns 0 for padding lanes' t = -1)
+template <typename F>
+__device__ __forceinline__ int batch_sum(const MainArgs& a, const BatchTiles& bt, F f) {
+  const int lane = threadIdx.x & 63;
+  int acc = lane < a.num_groups ? f(bt.t) : 0;
+  if (!bt.small) {
+    for (int i = 64 + lane; i < a.num_groups; i += 64) acc += f(seq_tiles(a, i));
+  }
+  return wave_sum_i(acc);
+}
+
+__device__ int dense_chunk(const MainArgs& a, const BatchTiles& bt) {
+  if (a.fixed_chunk > 0) return a.fixed_chunk;
+  const int G = a.num_groups, P = a.split_slots;
+  const int tsum = batch_sum(a, bt, [](int t) { return t; });  // the host keeps B x tiles < 2^31
+  const int tmax = wave_max_i(bt.small ? bt.t : [&] {
+    int m = bt.t;
+    for (int i = 64 + (int)(threadIdx.x & 63); i < G; i += 64) m = max(m, seq_tiles(a, i));
+    return m;
+  }());
+  int lo = max(kMinChunkDense, max((tsum + P - 1) / P, (tmax + kMaxSplits - 1) / kMaxSplits));
+  // C = ceil(sum t / (P - G)) always fits: sum ceil(t_b / C) <= sum t_b / C + G <= P.
+  int hi = P > G ? (tsum + (P - G) - 1) / (P - G) : max(tmax, 1);
+  hi = max(hi, lo);
+  while (lo < hi) {  // smallest chunk in [lo, hi] whose slots fit
+    const int mid = lo + ((hi - lo) >> 1);
+    const int need = batch_sum(a, bt, [mid](int t) { return seq_slots(t, mid); });
+    if (need <= P) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// The split a dense slot belongs to. group < 0: the slot is unused.
+struct DenseSlot {
+  int group, split;
+  int n_slots;  // slots of the group
+};
+
+__device__ DenseSlot dense_slot(const MainArgs& a, const BatchTiles& bt, int chunk, int slot) {
+  const int lane = threadIdx.x & 63;
+  const int G = a.num_groups;
+  DenseSlot r = {-1, 0, 0};
+  int base = 0;
+  for (int i0 = 0; i0 < G; i0 += 64) {
+    const int i = i0 + lane;
+    const int t = i0 == 0 ? bt.t : (i < G ? seq_tiles(a, i) : 0);
+    const int n = i < G ? seq_slots(t, chunk) : 0;
+    int incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    incl += base;
+    const int excl = incl - n;
+    const uint64_t hit = __ballot(i < G && excl <= slot && slot < incl);
+    if (hit != 0ull) {
+      const int src = __builtin_ctzll(hit);
+      r.group = uniform(__shfl(i, src));
+      r.n_slots = uniform(__shfl(n, src));
+      r.split = slot - uniform(__shfl(excl, src));
+      return r;
+    }
+    base = uniform(__shfl(incl, 63));
+  }
+  return r;
+}
+
+// Tiles per split and splits holding keys for a group of t tiles over n slots.
+__device__ __forceinline__ void spread_tiles(int t, int n, int& chunk, int& active) {
+  chunk = t > 0 ? (t + n - 1) / n : 1;
+  active = t > 0 ? (t + chunk - 1) / chunk : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -176,18 +297,54 @@ mla_split_kernel(MainArgs a) {
   const int half = lane >> 5;  // which 16-key half of the 32x32 accumulator a lane holds
   const int l32 = lane & 31;
 
-  const int sg = a.num_splits * a.num_groups;
+  // Block -> (row block, split, query group). Sparse: bid = rb*(S*G) + split*G +
+  // group, uniform splits. Dense: bid = rb*slots + slot, the slot decoded by the
+  // device plan. Workgroups are dealt to the 8 XCDs round-robin, so when the
+  // stride (S*G or slots) is a multiple of 8, as in the long single-sequence
+  // case, all row blocks of one KV chunk share one XCD's L2. (Padding other
+  // strides to a multiple of 8 measured slower for short sequences.)
   const int bid = blockIdx.x;
-  const int rb = bid / sg;
-  const int rem = bid - rb * sg;
-  const int split = rem / a.num_groups;
-  const int group = rem - split * a.num_groups;
+  int rb, split, group, chunk, n_active;
+  int64_t rec_slot;  // workspace record of (rb, split, group), before the wave index
+  if (kSparseMode) {
+    const int sg = a.num_splits * a.num_groups;
+    rb = bid / sg;
+    const int rem = bid - rb * sg;
+    split = rem / a.num_groups;
+    group = rem - split * a.num_groups;
+    chunk = a.chunk_tiles;
+    n_active = min(a.num_splits, (group_info(a, group, true).n_tiles + chunk - 1) / chunk);
+    rec_slot = ((int64_t)split * a.num_groups + group) * a.row_blocks + rb;
+  } else {
+    rb = bid / a.slot_stride;
+    const int slot = bid - rb * a.slot_stride;
+    if (slot >= a.split_slots) return;
+    if (a.num_groups == 1) {
+      // One sequence: all slots are its splits, at the host's chunk (no search).
+      group = 0;
+      split = slot;
+      chunk = a.chunk_tiles;
+      n_active = min(a.split_slots, (group_info(a, 0, false).n_tiles + chunk - 1) / chunk);
+    } else {
+      const BatchTiles bt = batch_tiles(a);
+      const DenseSlot ds = dense_slot(a, bt, dense_chunk(a, bt), slot);
+      if (ds.group < 0) return;  // slot left over by the plan
+      group = ds.group;
+      split = ds.split;
+      spread_tiles(group_info(a, group, false).n_tiles, ds.n_slots, chunk, n_active);
+      if (split == 0 && rb == 0 && threadIdx.x == 0 && a.ws_meta != nullptr)
+        a.ws_meta[group] = make_int2(slot, n_active);  // the combine's map to this group's records
+    }
+    rec_slot = (int64_t)slot * a.row_blocks + rb;
+  }
+  // One split holding all of a group's keys writes out/lse itself.
+  const bool direct = a.final_out != 0 || n_active <= 1;
 
   const GroupInfo gi = group_info(a, group, kSparseMode);
   const int b = gi.b;
   const int kv_len = gi.kv_len;
-  const int t_begin = split * a.chunk_tiles;
-  const int t_end = min(t_begin + a.chunk_tiles, gi.n_tiles);
+  const int t_begin = split * chunk;
+  const int t_end = min(t_begin + chunk, gi.n_tiles);
 
   const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave;
   const bool wave_active = row0 < a.rows_per_group;
@@ -196,8 +353,9 @@ mla_split_kernel(MainArgs a) {
   const int64_t qrow = (int64_t)group * a.rows_per_group + row;
 
   if (t_begin >= t_end) {
-    // No keys for this group at all (only reachable with a single split): empty softmax.
-    if (a.final_out && split == 0 && row_valid) {
+    // No keys for this group at all: empty softmax (a trailing empty split of a
+    // group with keys elsewhere writes nothing; the combine skips it).
+    if (direct && split == 0 && row_valid) {
       uint2 z = {0u, 0u};
       for (int d = 4 * half; d < kDL; d += 8)
         *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = z;
@@ -615,7 +773,7 @@ mla_split_kernel(MainArgs a) {
   const bool live = l_row > 0.f;
   const float inv = live && lq_row > 0.f ? 1.0f / lq_row : 0.f;
   const float lse2 = live ? m_ref + fast_log2(l_row) : -__builtin_inff();
-  if (a.final_out) {
+  if (direct) {
     if (row_valid) {
       uint16_t* dst = a.out + qrow * kDL;
 #pragma unroll
@@ -634,8 +792,7 @@ mla_split_kernel(MainArgs a) {
       if (half == 0) a.lse[qrow] = live ? lse2 * kLn2 : -__builtin_inff();
     }
   } else {
-    const int64_t rec =
-        (((int64_t)split * a.num_groups + group) * a.row_blocks + rb) * kWaves + wave;
+    const int64_t rec = rec_slot * kWaves + wave;
     // fp16 with a per-row power-of-two scale keeps 11 significant bits of the
     // normalised partial (|o| <= the largest value-row entry) at half the bytes.
     float amax = 0.f;
@@ -699,9 +856,26 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;  // padding wave record
 
   const GroupInfo gi = group_info(a, group, kSparseMode);
-  const int n_active = min(a.num_splits, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
-  const int64_t rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
-  const int64_t rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
+  int n_active;
+  int64_t rec0, rec_stride;  // record of split 0 of this (group, rb, wave); step per split
+  if (kSparseMode) {
+    n_active = min(a.num_splits, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
+    rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
+    rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
+  } else {
+    int slot0;
+    if (a.num_groups == 1) {
+      slot0 = 0;
+      n_active = min(a.split_slots, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
+    } else {
+      const int2 m = a.ws_meta[group];  // written by the split kernel
+      slot0 = m.x;
+      n_active = m.y;
+    }
+    rec0 = ((int64_t)slot0 * a.row_blocks + rb) * kWaves + wave;
+    rec_stride = (int64_t)a.row_blocks * kWaves;
+  }
+  if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
   const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
 
   // ---- phase 1: per-row maxima, sums and weights (thread = row x split lane) ----
@@ -782,7 +956,10 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
 // ---------------------------------------------------------------------------
 template <int MODE>
 static hipError_t launch_split(const MainArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)a.row_blocks * (unsigned)a.num_splits * (unsigned)a.num_groups;
+  constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
+  const unsigned grid = kSparseMode
+                            ? (unsigned)a.row_blocks * (unsigned)a.num_splits * (unsigned)a.num_groups
+                            : (unsigned)a.row_blocks * (unsigned)a.slot_stride;
   hipLaunchKernelGGL(mla_split_kernel<MODE>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

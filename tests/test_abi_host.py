@@ -81,6 +81,8 @@ def call(lib, dims, sparse=False, ptrs=None, ws=None, ws_bytes=0, scale=0.1):
     dict(kw=dict(kv_seq_stride=100)),       # stride < max_kv_len
     dict(kw=dict(batch=2)),                 # second sequence past kv_rows
     dict(kw=dict(num_splits=-1)),
+    dict(kw=dict(batch=40000, max_kv_len=1 << 22, kv_seq_stride=1 << 22,
+                 kv_rows=40000 << 22)),  # batch x tiles past 2^31
     dict(kw=dict(phase=3)),
     dict(ptrs=dict(q_lat=None)),
     dict(ptrs=dict(out=None)),
@@ -132,7 +134,8 @@ def test_plan_shapes():
     p = mv.plan(d)
     assert (p.row_blocks, p.num_groups, p.rows_per_group) == (8, 1, 1024)
     assert p.num_splits * p.chunk_tiles >= 1025 > (p.num_splits - 1) * p.chunk_tiles
-    assert p.workspace_bytes == p.num_splits * 8 * 4 * (32 * 512 * 2 + 3 * 32 * 4)
+    assert p.split_slots == p.num_splits == 32
+    assert p.workspace_bytes == p.split_slots * 8 * 4 * (32 * 512 * 2 + 3 * 32 * 4)
     # tiny chain: one split, no workspace
     p1 = mv.plan(_dims())
     assert p1.num_splits == 1 and p1.workspace_bytes == 0
@@ -148,6 +151,26 @@ def test_plan_shapes():
     assert p7.num_splits == 7 and p7.chunk_tiles == 2
     p8 = mv.plan(_dims(num_splits=50))
     assert p8.num_splits == 3  # 132 keys = 3 tiles
+
+
+def test_plan_ragged_batch_slots():
+    # A ragged batch gets slots for one workgroup per CU; the kernels share them
+    # out by the actual lengths, so the plan no longer multiplies by the batch.
+    d = _dims(batch=8, num_q=8, num_heads=64, max_kv_len=30186, kv_rows=8 * 30186,
+              kv_seq_stride=30186)
+    p = mv.plan(d)
+    assert (p.row_blocks, p.num_groups) == (4, 8)
+    assert p.split_slots == 64  # 256 CUs / 4 row blocks
+    # records, then one (first slot, splits) pair per sequence for the combine
+    assert p.workspace_bytes == 64 * 4 * 4 * (32 * 512 * 2 + 3 * 32 * 4) + 8 * 8
+    # a requested split count is per sequence
+    p2 = mv.plan(_dims(batch=8, num_q=8, num_heads=64, max_kv_len=30186, kv_rows=8 * 30186,
+                       kv_seq_stride=30186, num_splits=3))
+    assert (p2.num_splits, p2.split_slots) == (3, 24)
+    # never fewer slots than sequences
+    p3 = mv.plan(_dims(batch=300, num_q=4, num_heads=64, max_kv_len=5000,
+                       kv_rows=300 * 5000, kv_seq_stride=5000))
+    assert p3.split_slots >= 300
 
 
 def test_strerror(lib):

@@ -49,6 +49,10 @@ SMALL = [
     Spec("contig_t1", B=3, T=1, H=64, layout="contig", prefix=[5, 64, 4000]),
     Spec("paged_small", B=3, T=8, H=64, layout="paged", prefix=[100, 1000, 3000]),
     Spec("paged_p128", B=2, T=3, H=32, layout="paged", prefix=[700, 190], page_size=128),
+    # ragged batches: the device split plan gives long sequences many splits,
+    # short ones one (written directly), and a sequence with no prefix at all
+    Spec("contig_skewed", B=4, T=3, H=64, layout="contig", prefix=[0, 9000, 40, 700]),
+    Spec("paged_skewed", B=6, T=4, H=32, layout="paged", prefix=[5000, 1, 130, 2500, 64, 12000]),
     Spec("sparse_small", B=4, T=2, H=64, layout="sparse", cache_len=5000, topk=300),
     Spec("sparse_h32_k70", B=2, T=3, H=32, layout="sparse", cache_len=900, topk=70),
     Spec("sparse_paged", B=2, T=2, H=64, layout="sparse", cache_len=3000, topk=200,
@@ -230,3 +234,50 @@ def test_late_large_score_takes_exact_second_pass(gpu_lib):
         ref_out, ref_lse = run_oracle(w)
         _check(out, lse, ref_out, ref_lse, tag=f"argmax splits={s}")
         assert np.abs(out[0, 0] - synth.bf16_bits_to_f64(w.c_kv[j])).max() < 1e-2
+
+
+def test_ragged_batch_with_empty_sequence(gpu_lib):
+    """kv_lens of 0 in a batch: that sequence's rows are out = 0, lse = -inf; the
+    device split plan still balances the others and they match the oracle."""
+    spec = Spec("ragged_empty", B=4, T=4, H=64, layout="paged", prefix=[3000, 200, 8000, 50])
+    w = generate(spec, seed=16)
+    w.kv_lens[1] = 0
+    _announce("ragged with an empty sequence", w)
+    d = _dev(w)
+    ref_out, ref_lse = run_oracle(w)
+    for splits in (0, 2):
+        d.run(num_splits=splits)
+        out, lse = d.results()
+        assert np.all(out[1] == 0.0) and np.all(lse[1] == -np.inf)
+        assert np.all(ref_lse[1] == -np.inf)
+        keep = [0, 2, 3]
+        _check(out[keep], lse[keep], ref_out[keep], ref_lse[keep], tag=f"ragged_empty s={splits}")
+
+
+def test_ragged_batch_equals_single_sequences(gpu_lib):
+    """Each sequence of a skewed batch gives the same result as when it is run
+    alone (the split plan only changes how keys are grouped, within tolerance)."""
+    spec = Spec("skew", B=3, T=2, H=64, layout="contig", prefix=[6000, 100, 2000])
+    w = generate(spec, seed=17)
+    _announce("ragged vs single", w)
+    d = _dev(w)
+    d.run()
+    out, lse = d.results()
+    ref_out, ref_lse = run_oracle(w)
+    _check(out, lse, ref_out, ref_lse, tag="skew batch")
+    for b in range(w.B):
+        sub = generate(Spec(f"skew{b}", B=1, T=2, H=64, layout="contig",
+                            prefix=int(w.kv_lens[b]) - w.T), seed=17)
+        # same rows as sequence b of the batch
+        sub.q_lat[:] = w.q_lat[b:b + 1]
+        sub.q_rope[:] = w.q_rope[b:b + 1]
+        r0 = b * w.kv_seq_stride
+        n = int(w.kv_lens[b])
+        sub.c_kv[:n] = w.c_kv[r0:r0 + n]
+        sub.k_rope[:n] = w.k_rope[r0:r0 + n]
+        sub.tree_mask[:] = w.tree_mask[b:b + 1]
+        ds = _dev(sub)
+        ds.run()
+        o1, l1 = ds.results()
+        assert np.abs(l1[0] - lse[b]).max() < 2e-4
+        assert np.abs(o1[0] - out[b]).max() <= OUT_TOL
