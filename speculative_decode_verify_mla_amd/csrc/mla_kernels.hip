@@ -364,44 +364,6 @@ mla_split_kernel(MainArgs a) {
     return;
   }
 
-  // ---- query rows into registers: the B operand of S^T = K Q^T ------------
-  // Lane (row l32, half h) holds dims 16c + 8h .. +7 of chunk c (c < 32: latent).
-  // Padding rows (past the group's rows) load row 0 of the group and are zeroed.
-  bf16x8 q[36];
-  {
-    const int64_t qsrc = row_valid ? qrow : (int64_t)group * a.rows_per_group;
-#pragma unroll
-    for (int c = 0; c < 36; ++c) {
-      const uint16_t* src = c < 32 ? a.q_lat + qsrc * kDL + 16 * c + 8 * half
-                                   : a.q_rope + qsrc * kDR + 16 * (c - 32) + 8 * half;
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(src);
-      q[c] = row_valid ? v : bf16x8{};
-    }
-  }
-
-  // ---- visibility of the T draft keys for this lane's row (dense) ----------
-  uint64_t vis = 0;
-  const int prefix = kv_len - a.T;
-  if (!kSparseMode && row_valid) {
-    const int t = row / a.H;
-    if (a.tree_mask != nullptr) {
-      // 16 independent byte loads per chunk, one wait per chunk
-      const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.T + t) * a.T;
-#pragma unroll
-      for (int j0 = 0; j0 < 64; j0 += 16) {
-        if (j0 < a.T) {
-          uint32_t m[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) m[j] = (j0 + j < a.T) ? mrow[j0 + j] : 0u;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) vis |= (uint64_t)(m[j] != 0u) << (j0 + j);
-        }
-      }
-    } else {
-      vis = (t >= 63) ? ~0ull : ((2ull << t) - 1ull);  // chain: drafts 0..t
-    }
-  }
-
   // ---- per-lane LDS read offsets ------------------------------------------
   // The swizzle XORs chunk-index bits that lie below a key row's base offset,
   // so every fragment offset is one per-lane base XOR a compile-time constant.
@@ -526,6 +488,83 @@ mla_split_kernel(MainArgs a) {
   };
   constexpr int kLoadsPerWave = 18;
 
+  // The first tile of the split (re-issued by a second pass). Dense: issued
+  // before the query loads so that its HBM latency overlaps theirs. (Sparse
+  // issues it in the pass loop: holding its index state across the query loads
+  // costs the gather loop spilled registers.)
+  int nv_cur = 0, nv_next = 0;
+  uint64_t vm_cur = 0, vm_next = 0;
+  int idx_next = -1;
+  auto issue_first_tile = [&]() {
+    TileLoad tl0;
+    nv_next = 0;
+    vm_next = 0;
+    if (kSparseMode) {
+      const int r0 = resolve_row(fetch_index(t_begin));
+      vm_cur = __ballot(r0 >= 0);
+      tl0 = prepare_sparse(r0, 0);
+      idx_next = t_begin + 1 < t_end ? fetch_index(t_begin + 1) : -1;
+    } else {
+      tl0 = prepare_dense(t_begin, 0, nv_cur);
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) load_one(tl0, i);
+  };
+  if (!kSparseMode) issue_first_tile();
+
+  // ---- query rows into registers: the B operand of S^T = K Q^T ------------
+  // Lane (row l32, half h) holds dims 16c + 8h .. +7 of chunk c (c < 32: latent).
+  // Padding rows (past the group's rows) compute a copy of the group's row 0;
+  // they are never written out.
+  bf16x8 q[36];
+  {
+    const int64_t qsrc = row_valid ? qrow : (int64_t)group * a.rows_per_group;
+#pragma unroll
+    for (int c = 0; c < 36; ++c) {
+      const uint16_t* src = c < 32 ? a.q_lat + qsrc * kDL + 16 * c + 8 * half
+                                   : a.q_rope + qsrc * kDR + 16 * (c - 32) + 8 * half;
+      q[c] = *reinterpret_cast<const bf16x8*>(src);
+    }
+  }
+
+  // ---- visibility of the T draft keys for this lane's row (dense) ----------
+  uint64_t vis = 0;
+  const int prefix = kv_len - a.T;
+  if (!kSparseMode && row_valid) {
+    const int t = row / a.H;
+    if (a.tree_mask != nullptr) {
+      const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.T + t) * a.T;
+      if ((a.T & 15) == 0 && (reinterpret_cast<uintptr_t>(a.tree_mask) & 15) == 0) {
+        // rows are 16-byte aligned: one load per 16 drafts
+#pragma unroll
+        for (int j0 = 0; j0 < 64; j0 += 16) {
+          if (j0 < a.T) {
+            const uint4 v = *reinterpret_cast<const uint4*>(mrow + j0);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              vis |= (uint64_t)(((w[j >> 2] >> (8 * (j & 3))) & 0xffu) != 0u) << (j0 + j);
+          }
+        }
+      } else {
+        // 16 independent byte loads per chunk, one wait per chunk
+#pragma unroll
+        for (int j0 = 0; j0 < 64; j0 += 16) {
+          if (j0 < a.T) {
+            uint32_t m[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) m[j] = (j0 + j < a.T) ? mrow[j0 + j] : 0u;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) vis |= (uint64_t)(m[j] != 0u) << (j0 + j);
+          }
+        }
+      }
+    } else {
+      vis = (t >= 63) ? ~0ull : ((2ull << t) - 1ull);  // chain: drafts 0..t
+    }
+  }
+
+
   // ---- softmax state ------------------------------------------------------------
   // The accumulator is never rescaled inside the loop: every exponent is taken
   // against a fixed per-row reference m_ref (the row max of the first half-tile
@@ -620,23 +659,7 @@ mla_split_kernel(MainArgs a) {
     lq_run = 0.f;
     bool overflow = false;
 
-    // ---- prologue --------------------------------------------------------------
-    int nv_cur = 0, nv_next = 0;
-    uint64_t vm_cur = 0, vm_next = 0;
-    int idx_next = -1;
-    {
-      TileLoad tl0;
-      if (kSparseMode) {
-        const int r0 = resolve_row(fetch_index(t_begin));
-        vm_cur = __ballot(r0 >= 0);
-        tl0 = prepare_sparse(r0, 0);
-        if (t_begin + 1 < t_end) idx_next = fetch_index(t_begin + 1);
-      } else {
-        tl0 = prepare_dense(t_begin, 0, nv_cur);
-      }
-#pragma unroll
-      for (int i = 0; i < kLoadsPerWave; ++i) load_one(tl0, i);
-    }
+    if (kSparseMode || pass > 0) issue_first_tile();  // stage 0 is free: a pass ends on a barrier
     if (threadIdx.x == 0) *restart_flag = 0;
 
     for (int tile = t_begin; tile < t_end; ++tile) {
@@ -878,6 +901,16 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
   const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
 
+  // The first 16 splits' partials (4 dims of one row per thread) are loaded
+  // before the weights are formed, so the two memory round trips overlap.
+  const int lane = t & 63, qq = t >> 6, half = lane >> 5, l32 = lane & 31;
+  const uint16_t* o_p = a.ws_o + rec0 * kRecElems + ((db * 4 + qq) * 64 + lane) * 4;
+  const int64_t o_step = rec_stride * kRecElems;
+  uint2 raw[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    raw[j] = j < n_active ? *reinterpret_cast<const uint2*>(o_p + j * o_step) : uint2{0u, 0u};
+
   // ---- phase 1: per-row maxima, sums and weights (thread = row x split lane) ----
   {
     const int r = t & 31, sl = t >> 5;  // 8 split lanes per row
@@ -922,16 +955,14 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   }
 
   // ---- phase 2: out = sum_s w_s o_s for 4 dims per thread -------------------------
-  const int lane = t & 63, qq = t >> 6, half = lane >> 5, l32 = lane & 31;
   const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
-  const uint16_t* o_p = a.ws_o + rec0 * kRecElems + ((db * 4 + qq) * 64 + lane) * 4;
-  const int64_t o_step = rec_stride * kRecElems;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < n_active; s0 += 16) {
-    uint2 raw[16];
+    if (s0 > 0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      raw[j] = s0 + j < n_active ? *reinterpret_cast<const uint2*>(o_p + (s0 + j) * o_step) : uint2{0u, 0u};
+      for (int j = 0; j < 16; ++j)
+        raw[j] = s0 + j < n_active ? *reinterpret_cast<const uint2*>(o_p + (s0 + j) * o_step) : uint2{0u, 0u};
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (s0 + j < n_active) {
