@@ -213,8 +213,11 @@ def main():
                                  topk=0 if idx is None else idx.shape[2], phase=0, **kw)
     info = mv.plan(dims, sparse=w.layout == "sparse")
     ws = torch.empty(max(int(info.workspace_bytes), 16), dtype=torch.uint8, device=dev)
-    log(f"plan: splits={info.num_splits} chunk_tiles={info.chunk_tiles} row_blocks={info.row_blocks} "
-        f"groups={info.num_groups} workgroups={info.num_splits*info.row_blocks*info.num_groups} "
+    # split-kernel grid: row blocks x (group, split) slots; dense slots are shared
+    # out on the device by the actual kv_lens
+    workgroups = int(info.split_slots) * int(info.row_blocks)
+    log(f"plan: split_slots={info.split_slots} (splits={info.num_splits} chunk_tiles={info.chunk_tiles} "
+        f"at max_kv_len) row_blocks={info.row_blocks} groups={info.num_groups} workgroups={workgroups} "
         f"workspace={info.workspace_bytes/1e6:.1f} MB; inputs x{len(copies)} copies")
     stream = torch.cuda.current_stream(dev)
 
@@ -307,8 +310,8 @@ def main():
                    "prefix": (w.kv_lens - w.T).tolist() if w.layout != "sparse" else None,
                    "kv_lens": w.kv_lens.tolist()[:8] if w.B <= 8 else f"{w.B} x {int(w.kv_lens[0])}",
                    "latent_dim": 512, "rope_dim": 64, "layout": w.layout,
-                   "topk": w.topk or None, "splits": int(info.num_splits),
-                   "workgroups": int(info.num_splits * info.row_blocks * info.num_groups)},
+                   "topk": w.topk or None, "split_slots": int(info.split_slots),
+                   "workgroups": workgroups},
         "achieved_hbm_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "warm_us_per_call": round(warm_us, 3),
