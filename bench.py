@@ -221,13 +221,14 @@ def main():
         f"workspace={info.workspace_bytes/1e6:.1f} MB; inputs x{len(copies)} copies")
     stream = torch.cuda.current_stream(dev)
 
-    def call(c, phase=mv.binding.PHASE_ALL):
+    def call(c, phase=mv.binding.PHASE_ALL, st=None):
+        st = stream if st is None else st
         if w.layout == "sparse":
             mv.sparse_attn(c["q_lat"], c["q_rope"], c["c_kv"], c["k_rope"], pt, idx, kv_lens,
-                           w.scale, out, lse, workspace=ws, stream=stream, phase=phase, **kw)
+                           w.scale, out, lse, workspace=ws, stream=st, phase=phase, **kw)
         else:
             mv.verify_attn(c["q_lat"], c["q_rope"], c["c_kv"], c["k_rope"], pt, mask, kv_lens,
-                           w.scale, out, lse, workspace=ws, stream=stream, phase=phase, **kw)
+                           w.scale, out, lse, workspace=ws, stream=st, phase=phase, **kw)
 
     # ---- warmup -----------------------------------------------------------------------
     for i in range(args.warmup):
@@ -254,6 +255,26 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     warm_us = t_start.elapsed_time(t_end) / K * 1e3
+
+    # ---- the same rotated calls replayed from one captured HIP graph -----------------------
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    call(copies[0], st=side)  # warm on the capture stream
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for c in copies:
+            call(c, st=side)
+    torch.cuda.synchronize()
+    reps = max(1, K // len(copies))
+    t_start.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    graph_us = t_start.elapsed_time(t_end) / (reps * len(copies)) * 1e3
+    log(f"graph replay: {graph_us:.2f} us/call ({reps} replays of {len(copies)} calls)")
+    del graph
 
     # ---- per-kernel durations: HIP events around each phase on the launch stream ------------
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -315,6 +336,7 @@ def main():
         "achieved_hbm_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "warm_us_per_call": round(warm_us, 3),
+        "graph_us_per_call": round(graph_us, 3),
         "split_kernel_us": round(split_ms * 1e3, 3),
         "combine_kernel_us": round(combine_ms * 1e3, 3),
         "algorithmic_bytes": int(wm["total_bytes"]),

@@ -44,12 +44,12 @@ class DeviceWorkload:
         self.lse = torch.empty((w.B, w.T, w.H), dtype=torch.float32, device=d)
 
     def run(self, num_splits=0, phase=mv.binding.PHASE_ALL, out=None, lse=None, q_lat=None,
-            q_rope=None):
+            q_rope=None, workspace=None, stream=None):
         w = self.w
         out = self.out if out is None else out
         lse = self.lse if lse is None else lse
         kw = dict(max_kv_len=w.max_kv_len, kv_seq_stride=w.kv_seq_stride, page_size=w.page_size,
-                  num_splits=num_splits, phase=phase)
+                  num_splits=num_splits, phase=phase, workspace=workspace, stream=stream)
         ql = self.q_lat if q_lat is None else q_lat
         qr = self.q_rope if q_rope is None else q_rope
         if w.layout == "sparse":
@@ -58,6 +58,16 @@ class DeviceWorkload:
         else:
             mv.verify_attn(ql, qr, self.c_kv, self.k_rope, self.page_table, self.tree_mask,
                            self.kv_lens, w.scale, out, lse, **kw)
+
+    def workspace(self, num_splits=0):
+        """A workspace of the size this workload's call needs (allocated here, not on capture)."""
+        w = self.w
+        dims = mv.binding._dims_from(self.q_lat, self.c_kv, self.kv_lens, max_kv_len=w.max_kv_len,
+                                     kv_seq_stride=w.kv_seq_stride, page_table=self.page_table,
+                                     page_size=w.page_size, topk=w.topk or 0,
+                                     num_splits=num_splits, phase=0)
+        n = mv.workspace_bytes(dims, sparse=w.layout == "sparse")
+        return torch.empty(max(n, 16), dtype=torch.uint8, device=self.device)
 
     def results(self, out=None, lse=None):
         torch.cuda.synchronize(self.device)

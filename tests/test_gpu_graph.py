@@ -1,0 +1,94 @@
+"""Serving-style use of the verify call: captured into a HIP graph and replayed,
+and issued on several streams at once. Every replay and every stream's result
+must equal the eager call bit for bit (the kernels are deterministic and the
+call keeps no state between launches)."""
+import numpy as np
+import pytest
+import torch
+
+from speculative_decode_verify_mla_amd import synth
+from speculative_decode_verify_mla_amd.synth import DL, Spec, generate
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("long_single", lambda: generate(Spec("g1", B=1, T=16, H=64, layout="contig", prefix=6000), seed=31)),
+    ("ragged_paged", lambda: generate(Spec("g2", B=4, T=4, H=64, layout="paged",
+                                           prefix=[5000, 40, 1200, 3000]), seed=32)),
+    ("sparse", lambda: generate(Spec("g3", B=4, T=1, H=64, layout="sparse", cache_len=8000,
+                                     topk=512), seed=33)),
+]
+
+
+def _dev(w):
+    from tests._gpu import DeviceWorkload
+    return DeviceWorkload(w)
+
+
+def _snapshot(d):
+    torch.cuda.synchronize()
+    return d.out.clone(), d.lse.clone()
+
+
+@pytest.mark.parametrize("name,make", CASES, ids=[c[0] for c in CASES])
+def test_graph_replay_equals_eager(gpu_lib, name, make):
+    w = make()
+    print(f"[case] graph replay {name} B={w.B} T={w.T} layout={w.layout}", flush=True)
+    d = _dev(w)
+    ws = d.workspace()
+    d.run(workspace=ws)
+    ref_out, ref_lse = _snapshot(d)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        d.run(workspace=ws, stream=side)  # warm on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        d.run(workspace=ws, stream=side)
+    torch.cuda.synchronize()
+
+    # other eager work between replays: scribble over the outputs and the
+    # workspace, and run an eager call with different queries
+    other_q = torch.flip(d.q_lat, dims=[2]).contiguous()
+    for rep in range(3):
+        d.out.fill_(0x7FC0)
+        d.lse.fill_(float("nan"))
+        ws.fill_(0xFF)
+        scratch_out = torch.empty_like(d.out)
+        scratch_lse = torch.empty_like(d.lse)
+        d.run(q_lat=other_q, out=scratch_out, lse=scratch_lse, workspace=ws)
+        torch.cuda.synchronize()
+        g.replay()
+        out, lse = _snapshot(d)
+        assert torch.equal(out, ref_out), f"replay {rep}: out differs"
+        assert torch.equal(lse, ref_lse), f"replay {rep}: lse differs"
+
+
+def test_streams_equal_eager(gpu_lib):
+    """Four calls in flight on four streams (own outputs and workspaces)."""
+    w = generate(Spec("ms", B=2, T=8, H=64, layout="contig", prefix=[3000, 7000]), seed=34)
+    print("[case] four streams", flush=True)
+    d = _dev(w)
+    n = 4
+    qs = [d.q_lat] + [torch.roll(d.q_lat, shifts=k, dims=2).contiguous() for k in range(1, n)]
+    outs = [torch.empty_like(d.out) for _ in range(n)]
+    lses = [torch.empty_like(d.lse) for _ in range(n)]
+    wss = [d.workspace() for _ in range(n)]
+    refs = []
+    for k in range(n):
+        d.run(q_lat=qs[k], out=outs[k], lse=lses[k], workspace=wss[k])
+        torch.cuda.synchronize()
+        refs.append((outs[k].clone(), lses[k].clone()))
+        outs[k].zero_()
+        lses[k].zero_()
+    streams = [torch.cuda.Stream() for _ in range(n)]
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for k in range(n):
+            streams[k].wait_stream(torch.cuda.current_stream())
+            d.run(q_lat=qs[k], out=outs[k], lse=lses[k], workspace=wss[k], stream=streams[k])
+        torch.cuda.synchronize()
+        for k in range(n):
+            assert torch.equal(outs[k], refs[k][0]) and torch.equal(lses[k], refs[k][1]), (rep, k)
