@@ -8,6 +8,8 @@ Contents:
   definition  – the plain masked-softmax definition in fp64 (the oracle proper),
                 plus the tile-streaming and chunk-combine forms of the same result.
   bruteforce  – pure-Python per-head loops with math.fsum, for tiny inputs.
+  compaction  – post-verify KV compaction (accepted draft rows moved to the
+                front of the draft region), the plain definition.
 
 Every function is pinned by tests under -m "not gpu" against brute force,
 a textbook attention routine (torch SDPA in float64), closed forms and
@@ -21,3 +23,4 @@ from .definition import (  # noqa: F401
     verify_dense,
     verify_sparse,
 )
+from .compaction import compact_kv  # noqa: F401
