@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic plan")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=("verify", "compact"), default="verify",
+                    help="verify: the attention call (default); compact: post-verify KV compaction")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (hardware counter scale)")
     args = ap.parse_args()
@@ -180,6 +182,9 @@ def main():
         return
     mv.load_library()
     log(f"device {torch.cuda.get_device_name(0)}; workload config {args.config}")
+    if args.op == "compact":
+        bench_compact(args, dev)
+        return
 
     w = synth.config(args.config)
     wm = work_model(w)
@@ -344,6 +349,84 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernel_source": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_compact(args, dev):
+    """Post-verify KV compaction on a dense workload: every sequence accepts a
+    root-to-node path of a random draft tree (parents drawn like the workload's)."""
+    import numpy as np
+    import torch
+
+    import speculative_decode_verify_mla_amd as mv
+    from speculative_decode_verify_mla_amd import synth
+
+    w = synth.config(args.config)
+    if w.layout == "sparse":
+        raise SystemExit("--op compact needs a dense (verify) workload")
+    rng = np.random.default_rng(1000 + args.config)
+    acc = np.full((w.B, w.T), -1, dtype=np.int32)
+    nacc = np.zeros(w.B, dtype=np.int32)
+    for b in range(w.B):
+        parents = synth.random_tree_parents(rng, w.T)
+        node, path = int(rng.integers(0, w.T)), []
+        while node >= 0:
+            path.append(node)
+            node = int(parents[node])
+        path = path[::-1]
+        acc[b, :len(path)] = path
+        nacc[b] = len(path)
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    c_kv, k_rope = u16(w.c_kv), u16(w.k_rope)
+    kv_lens = torch.from_numpy(w.kv_lens.astype(np.int32)).to(dev)
+    pt = None if w.page_table is None else torch.from_numpy(w.page_table.astype(np.int32)).to(dev)
+    acc_t, n_t = torch.from_numpy(acc).to(dev), torch.from_numpy(nacc).to(dev)
+    new_lens = torch.empty_like(kv_lens)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        mv.compact_kv(c_kv, k_rope, pt, kv_lens, acc_t, n_t, new_lens, max_kv_len=w.max_kv_len,
+                      kv_seq_stride=w.kv_seq_stride, page_size=w.page_size, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / K * 1e3
+    moved = int(sum(max(0, min(int(n), w.T)) for n in nacc)) * (LATENT_ROW_BYTES + ROPE_ROW_BYTES)
+    alg_bytes = 2 * moved + 4 * w.B * (w.T + 3)  # rows read + written, indices and lengths
+    gbps = alg_bytes / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_budget, 5.0):
+            oracle.compact_kv(w.c_kv, w.k_rope, w.kv_lens, acc, nacc, w.T, kv_seq_stride=w.kv_seq_stride,
+                              page_table=w.page_table, page_size=w.page_size, max_kv_len=w.max_kv_len)
+            reps += 1
+        el = time.perf_counter() - t0
+        cpu = dict(value=el / reps * 1e6, unit="us/call", cores=1, kind="oracle",
+                   sample=f"{reps} whole calls of the numpy oracle (it copies the cache once per call)")
+    line = {
+        "metric": "kv-compaction µs/call (post-verify, accepted path to the front of the draft region)",
+        "value": round(us, 3), "unit": "us/call", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u16", "data": "synthetic (seeded), root-to-node accepted paths",
+        "config": {"workload": w.spec.name, "batch": w.B, "draft_tokens": w.T,
+                   "accepted": nacc.tolist()},
+        "algorithmic_bytes": alg_bytes, "achieved_hbm_GBps": round(gbps, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 5), "traffic": None,
+                     "kernel": "mla_compact_kernel"},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

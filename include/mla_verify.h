@@ -159,6 +159,33 @@ int mla_sparse_attn(const mla_dims* dims, const uint16_t* q_lat, const uint16_t*
                     uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Post-verify KV compaction. "The Shared Memory Ceiling", section "The Broader
+ * Context: Building a Custom sm_120 Verify Kernel", names a "defrag" step after
+ * verification; its plain reading: the cache rows of the accepted draft tokens
+ * move, in path order, to the front of the draft region, so the next decoding
+ * step sees prefix + accepted tokens as one contiguous run.
+ *
+ * For sequence b: kv = kv_lens[b] clamped to [0, max_kv_len], P = kv - T,
+ * n = num_accepted[b] clamped to [0, T], and for i < n
+ *     row(P + i) <- row(P + accepted[b, i])        (c_kv and k_rope rows)
+ *     new_kv_lens[b] = max(P + n, 0).
+ * Every source row is read before any destination row is written, so moves
+ * that overlap are well defined (a root-to-node path has accepted[b,i] >= i;
+ * any order is accepted). A move is skipped when its draft index is outside
+ * [0, T), either position is outside [0, kv), or either physical row is absent
+ * (page-table entry < 0 or row >= kv_rows). Rows of other positions are not
+ * touched. Sequences must not share the pages that hold their draft regions.
+ *
+ * dims: the verify call's dims (batch, num_q = T, page_size, max_pages,
+ * max_kv_len, kv_seq_stride, kv_rows; the same checks as mla_verify_attn).
+ * c_kv bf16 [kv_rows, 512] and k_rope bf16 [kv_rows, 64] are updated in place
+ * (16-byte aligned); accepted i32 [B, T], num_accepted i32 [B], new_kv_lens
+ * i32 [B] (may alias kv_lens), all 4-byte aligned device memory. Enqueued on
+ * `stream`; no workspace. Returns MLA_OK or a negative MLA_ERR_* code. */
+int mla_compact_kv(const mla_dims* dims, uint16_t* c_kv, uint16_t* k_rope,
+                   const int32_t* page_table, const int32_t* kv_lens, const int32_t* accepted,
+                   const int32_t* num_accepted, int32_t* new_kv_lens, void* stream);
+
 /* Static description of an error code (never NULL). */
 const char* mla_verify_strerror(int code);
 

@@ -31,6 +31,7 @@ EXPORTED = (
     "mla_verify_attn",
     "mla_sparse_attn",
     "mla_verify_strerror",
+    "mla_compact_kv",
 )
 
 
@@ -95,6 +96,8 @@ def load_library(path: Optional[str] = None):
         lib.mla_verify_attn.restype = i32
         lib.mla_sparse_attn.argtypes = common
         lib.mla_sparse_attn.restype = i32
+        lib.mla_compact_kv.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.mla_compact_kv.restype = i32
         lib.mla_verify_strerror.argtypes = [i32]
         lib.mla_verify_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -211,3 +214,27 @@ def sparse_attn(q_lat, q_rope, c_kv, k_rope, page_table, indices, kv_lens, scale
     _call("mla_sparse_attn", dims, True, _as_u16(q_lat), _as_u16(q_rope), _as_u16(c_kv),
           _as_u16(k_rope), page_table, indices, kv_lens, scale, _as_u16(out), lse, workspace,
           stream)
+
+
+def compact_kv(c_kv, k_rope, page_table, kv_lens, accepted, num_accepted, new_kv_lens, *,
+               max_kv_len: int, kv_seq_stride: int = 0, page_size: int = 0, stream=None):
+    """Post-verify KV compaction (mla_compact_kv), in place on c_kv / k_rope.
+
+    accepted is int32 [B, T] (draft indices in path order), num_accepted int32 [B];
+    new_kv_lens int32 [B] receives the compacted lengths (it may be kv_lens itself).
+    """
+    import torch
+
+    B, T = accepted.shape
+    dims = make_dims(batch=int(B), num_q=int(T), num_heads=1, max_kv_len=int(max_kv_len),
+                     kv_rows=int(c_kv.shape[0]), kv_seq_stride=int(kv_seq_stride),
+                     page_size=int(page_size) if page_table is not None else 0,
+                     max_pages=int(page_table.shape[1]) if page_table is not None else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(c_kv.device)
+    rc = load_library().mla_compact_kv(ctypes.byref(dims), _ptr(_as_u16(c_kv)), _ptr(_as_u16(k_rope)),
+                                       _ptr(page_table), _ptr(kv_lens), _ptr(accepted),
+                                       _ptr(num_accepted), _ptr(new_kv_lens),
+                                       ctypes.c_void_p(stream.cuda_stream))
+    if rc != MLA_OK:
+        raise MlaError(rc, "mla_compact_kv")

@@ -254,6 +254,40 @@ int mla_sparse_attn(const mla_dims* dims, const uint16_t* q_lat, const uint16_t*
              scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+int mla_compact_kv(const mla_dims* dims, uint16_t* c_kv, uint16_t* k_rope,
+                   const int32_t* page_table, const int32_t* kv_lens, const int32_t* accepted,
+                   const int32_t* num_accepted, int32_t* new_kv_lens, void* stream) {
+  if (dims == nullptr) return MLA_ERR_INVALID;
+  if ((page_table != nullptr) != (dims->page_size != 0)) return MLA_ERR_INVALID;
+  int rc = check_dims(dims, false, page_table != nullptr);
+  if (rc != MLA_OK) return rc;
+  if (!c_kv || !k_rope || !kv_lens || !accepted || !num_accepted || !new_kv_lens)
+    return MLA_ERR_INVALID;
+  if (!aligned(c_kv, 16) || !aligned(k_rope, 16) || !aligned(kv_lens, 4) || !aligned(accepted, 4) ||
+      !aligned(num_accepted, 4) || !aligned(new_kv_lens, 4) || (page_table && !aligned(page_table, 4)))
+    return MLA_ERR_INVALID;
+  rc = check_device();
+  if (rc != MLA_OK) return rc;
+  mlav::CompactArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.c_kv = c_kv;
+  a.k_rope = k_rope;
+  a.page_table = page_table;
+  a.kv_lens = kv_lens;
+  a.accepted = accepted;
+  a.num_accepted = num_accepted;
+  a.new_kv_lens = new_kv_lens;
+  a.kv_seq_stride = page_table ? 0 : dims->kv_seq_stride;
+  a.kv_rows = dims->kv_rows;
+  a.T = dims->num_q;
+  a.page_size = page_table ? dims->page_size : 0;
+  a.max_pages = page_table ? dims->max_pages : 0;
+  a.max_kv_len = dims->max_kv_len;
+  if (mlav::launch_compact_kernel(a, dims->batch, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_verify_strerror(int code) {
   switch (code) {
     case MLA_OK: return "success";

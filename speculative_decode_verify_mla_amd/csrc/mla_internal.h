@@ -64,6 +64,24 @@ struct MainArgs {
   float scale_log2;    // scale * log2(e)
 };
 
+// Post-verify KV compaction (mla_compact.hip).
+struct CompactArgs {
+  uint16_t* c_kv;
+  uint16_t* k_rope;
+  const int32_t* page_table;
+  const int32_t* kv_lens;
+  const int32_t* accepted;      // [B, T] draft indices in path order
+  const int32_t* num_accepted;  // [B]
+  int32_t* new_kv_lens;         // [B], may alias kv_lens
+  int64_t kv_seq_stride;
+  int64_t kv_rows;
+  int32_t T;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t max_kv_len;
+};
+hipError_t launch_compact_kernel(const CompactArgs& a, int batch, hipStream_t stream);
+
 // Launchers (defined in mla_kernels.hip). Return the hipError_t of the launch.
 hipError_t launch_split_kernel(const MainArgs& a, int mode, hipStream_t stream);
 hipError_t launch_combine_kernel(const MainArgs& a, int mode, hipStream_t stream);

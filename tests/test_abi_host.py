@@ -177,3 +177,21 @@ def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, 99):
         assert isinstance(lib.mla_verify_strerror(code), bytes)
     assert mv.strerror(B.MLA_ERR_WORKSPACE) == "workspace missing or too small"
+
+
+def test_compact_invalid_arguments(lib):
+    d = _dims(batch=2, num_q=4, max_kv_len=132, kv_rows=264, kv_seq_stride=132)
+    ok = dict(c=P(), r=P(), pt=None, kv=P(), acc=P(), n=P(), new=P())
+
+    def call_c(dims, **kw):
+        p = dict(ok, **kw)
+        return lib.mla_compact_kv(ctypes.byref(dims) if dims is not None else None, p["c"], p["r"],
+                                  p["pt"], p["kv"], p["acc"], p["n"], p["new"], None)
+
+    assert call_c(None) == B.MLA_ERR_INVALID
+    for k in ("c", "r", "kv", "acc", "n", "new"):
+        assert call_c(d, **{k: None}) == B.MLA_ERR_INVALID, k
+    assert call_c(d, c=MIS()) == B.MLA_ERR_INVALID
+    assert call_c(d, pt=P()) == B.MLA_ERR_INVALID  # page table without a page size
+    assert call_c(_dims(batch=2, num_q=65, max_kv_len=132, kv_rows=264, kv_seq_stride=132)) == \
+        B.MLA_ERR_INVALID
