@@ -10,6 +10,7 @@ Contents:
   bruteforce  – pure-Python per-head loops with math.fsum, for tiny inputs.
   compaction  – post-verify KV compaction (accepted draft rows moved to the
                 front of the draft region), the plain definition.
+  projection  – per-head projections into and out of the latent space.
 
 Every function is pinned by tests under -m "not gpu" against brute force,
 a textbook attention routine (torch SDPA in float64), closed forms and
@@ -24,3 +25,4 @@ from .definition import (  # noqa: F401
     verify_sparse,
 )
 from .compaction import compact_kv  # noqa: F401
+from .projection import head_project  # noqa: F401
