@@ -29,6 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 LATENT_ROW_BYTES = 512 * 2
 ROPE_ROW_BYTES = 64 * 2
 KERNEL_SOURCES = ("speculative_decode_verify_mla_amd/csrc/mla_kernels.hip",
+                  "speculative_decode_verify_mla_amd/csrc/mla_device.h",
                   "speculative_decode_verify_mla_amd/csrc/mla_api.hip",
                   "speculative_decode_verify_mla_amd/csrc/mla_internal.h")
 
@@ -149,8 +150,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic plan")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("verify", "compact"), default="verify",
-                    help="verify: the attention call (default); compact: post-verify KV compaction")
+    ap.add_argument("--op", choices=("verify", "compact", "proj"), default="verify",
+                    help="verify: the attention call (default); compact: post-verify KV "
+                         "compaction; proj: the per-head projections around it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (hardware counter scale)")
     args = ap.parse_args()
@@ -184,6 +186,9 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}; workload config {args.config}")
     if args.op == "compact":
         bench_compact(args, dev)
+        return
+    if args.op == "proj":
+        bench_proj(args, dev)
         return
 
     w = synth.config(args.config)
@@ -353,6 +358,43 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def _time_small_op(fn, steps, warmup, dev):
+    """(eager us/call, graph us/call) of a small launch-bound op: eager is
+    limited by host enqueue (Python + ctypes), the graph replays `steps`
+    captured calls with no host work in between (the kernels' own rate)."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(warmup):
+        fn(i, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) / steps * 1e3
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    fn(0, side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(steps):
+            fn(i, side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph = e0.elapsed_time(e1) / steps * 1e3
+    del g
+    return eager, graph
+
+
 def bench_compact(args, dev):
     """Post-verify KV compaction on a dense workload: every sequence accepts a
     root-to-node path of a random draft tree (parents drawn like the workload's)."""
@@ -385,21 +427,13 @@ def bench_compact(args, dev):
     new_lens = torch.empty_like(kv_lens)
     stream = torch.cuda.current_stream(dev)
 
-    def call():
+    def call(i, st):
         mv.compact_kv(c_kv, k_rope, pt, kv_lens, acc_t, n_t, new_lens, max_kv_len=w.max_kv_len,
-                      kv_seq_stride=w.kv_seq_stride, page_size=w.page_size, stream=stream)
+                      kv_seq_stride=w.kv_seq_stride, page_size=w.page_size, stream=st)
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
     K = args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(K):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / K * 1e3
+    eager_us, us = _time_small_op(call, K, args.warmup, dev)
+    log(f"compaction: {us:.2f} us/call from a captured graph, {eager_us:.2f} us/call eager")
     moved = int(sum(max(0, min(int(n), w.T)) for n in nacc)) * (LATENT_ROW_BYTES + ROPE_ROW_BYTES)
     alg_bytes = 2 * moved + 4 * w.B * (w.T + 3)  # rows read + written, indices and lengths
     gbps = alg_bytes / (us * 1e-6) / 1e9
@@ -423,10 +457,58 @@ def bench_compact(args, dev):
         "config": {"workload": w.spec.name, "batch": w.B, "draft_tokens": w.T,
                    "accepted": nacc.tolist()},
         "algorithmic_bytes": alg_bytes, "achieved_hbm_GBps": round(gbps, 2),
+        "eager_us_per_call": round(eager_us, 3), "timing": "graph replay of the timed calls",
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 5), "traffic": None,
                      "kernel": "mla_compact_kernel"},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_proj(args, dev):
+    """Query absorption (q_nope . W_UK, 128 -> 512) and per-head output
+    (out_lat . W_UV, 512 -> 128) for one verify step of the workload's tokens."""
+    import numpy as np
+    import torch
+
+    import speculative_decode_verify_mla_amd as mv
+    from speculative_decode_verify_mla_amd import synth
+
+    w = synth.config(args.config)
+    M, H = w.B * w.T, w.H
+    rng = np.random.default_rng(2000 + args.config)
+    bf = lambda shape, sc=1.0: torch.from_numpy(synth.f32_to_bf16_bits(
+        (rng.standard_normal(shape) * sc).astype(np.float32)).view(np.int16)).to(dev)
+    res = {}
+    for name, K, N in (("absorb_q", 128, 512), ("head_out", 512, 128)):
+        copies = [(bf((M, H, K)), bf((H, K, N), 1 / np.sqrt(K))) for _ in range(max(args.copies, 1))]
+        y = torch.empty((M, H, N), dtype=torch.int16, device=dev)
+
+        def call(i, st, copies=copies, y=y):
+            mv.head_project(*copies[i % len(copies)], y, stream=st)
+
+        eager_us, us = _time_small_op(call, args.steps, args.warmup, dev)
+        nbytes = 2 * (M * H * K + H * K * N + M * H * N)
+        res[name] = dict(us=round(us, 3), eager_us=round(eager_us, 3), bytes=nbytes,
+                         GBps=round(nbytes / (us * 1e-6) / 1e9, 1), flops=2 * M * H * K * N)
+        log(f"{name}: M={M} H={H} {K}->{N}: {us:.2f} us (graph), {eager_us:.2f} us eager, "
+            f"{res[name]['GBps']} GB/s")
+    tot_us = res["absorb_q"]["us"] + res["head_out"]["us"]
+    tot_b = res["absorb_q"]["bytes"] + res["head_out"]["bytes"]
+    gbps = tot_b / (tot_us * 1e-6) / 1e9
+    line = {
+        "metric": "absorbed-MLA projections µs per verify step (q_nope.W_UK + out_lat.W_UV)",
+        "value": round(tot_us, 3), "unit": "us/step", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(tot_us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": w.spec.name, "tokens": M, "heads": H, "copies": len(copies)},
+        "timing": "graph replay of the timed calls (weights rotate over the copies)",
+        "kernels": res,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "mla_proj_kernel"},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

@@ -186,6 +186,24 @@ int mla_compact_kv(const mla_dims* dims, uint16_t* c_kv, uint16_t* k_rope,
                    const int32_t* page_table, const int32_t* kv_lens, const int32_t* accepted,
                    const int32_t* num_accepted, int32_t* new_kv_lens, void* stream);
 
+/* Per-head projection around absorbed attention: for every token m and head h
+ *     y[m, h, :] = x[m, h, :] . w[h]          (w[h] is in_dim x out_dim)
+ * in bf16 with fp32 accumulation and a round-to-nearest-even bf16 result.
+ * Absorbed MLA ("The Shared Memory Ceiling", section "The Broader Context:
+ * Building a Custom sm_120 Verify Kernel": attention over the shared MLA
+ * latent) uses it on both sides of mla_verify_attn: the query absorption
+ * q_lat = q_nope . W_UK (in_dim 128, out_dim 512) and the per-head output
+ * o = out . W_UV (in_dim 512, out_dim 128).
+ *
+ * x bf16 [tokens, heads, in_dim], w bf16 [heads, in_dim, out_dim], y bf16
+ * [tokens, heads, out_dim], row-major, 16-byte aligned device memory, caller
+ * owned; y must not overlap x or w. Checks (MLA_ERR_INVALID): tokens >= 1,
+ * heads >= 1, in_dim a multiple of 16 in [16, 1024], out_dim a multiple of 32,
+ * in_dim * out_dim < 2^30, tokens * heads * max(in_dim, out_dim) < 2^40.
+ * Enqueued on `stream`; no workspace. */
+int mla_head_project(int32_t tokens, int32_t heads, int32_t in_dim, int32_t out_dim,
+                     const uint16_t* x, const uint16_t* w, uint16_t* y, void* stream);
+
 /* Static description of an error code (never NULL). */
 const char* mla_verify_strerror(int code);
 

@@ -7,6 +7,7 @@ tensors into that ABI; ``synth`` draws seeded synthetic inputs.
 from .binding import (  # noqa: F401
     MlaError,
     compact_kv,
+    head_project,
     load_library,
     plan,
     sparse_attn,

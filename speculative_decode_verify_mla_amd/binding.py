@@ -32,6 +32,7 @@ EXPORTED = (
     "mla_sparse_attn",
     "mla_verify_strerror",
     "mla_compact_kv",
+    "mla_head_project",
 )
 
 
@@ -98,6 +99,8 @@ def load_library(path: Optional[str] = None):
         lib.mla_sparse_attn.restype = i32
         lib.mla_compact_kv.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.mla_compact_kv.restype = i32
+        lib.mla_head_project.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+        lib.mla_head_project.restype = i32
         lib.mla_verify_strerror.argtypes = [i32]
         lib.mla_verify_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -238,3 +241,21 @@ def compact_kv(c_kv, k_rope, page_table, kv_lens, accepted, num_accepted, new_kv
                                        ctypes.c_void_p(stream.cuda_stream))
     if rc != MLA_OK:
         raise MlaError(rc, "mla_compact_kv")
+
+
+def head_project(x, w, y, stream=None):
+    """y[m, h, :] = x[m, h, :] . w[h] (mla_head_project): x [tokens, heads, in_dim],
+    w [heads, in_dim, out_dim], y [tokens, heads, out_dim], all bf16 (or uint16)."""
+    import torch
+
+    M, H, K = x.shape
+    N = w.shape[2]
+    if tuple(w.shape) != (H, K, N) or tuple(y.shape) != (M, H, N):
+        raise ValueError("head_project: x [M,H,K], w [H,K,N], y [M,H,N]")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    rc = load_library().mla_head_project(int(M), int(H), int(K), int(N), _ptr(_as_u16(x)),
+                                         _ptr(_as_u16(w)), _ptr(_as_u16(y)),
+                                         ctypes.c_void_p(stream.cuda_stream))
+    if rc != MLA_OK:
+        raise MlaError(rc, "mla_head_project")

@@ -288,6 +288,29 @@ int mla_compact_kv(const mla_dims* dims, uint16_t* c_kv, uint16_t* k_rope,
   return MLA_OK;
 }
 
+int mla_head_project(int32_t tokens, int32_t heads, int32_t in_dim, int32_t out_dim,
+                     const uint16_t* x, const uint16_t* w, uint16_t* y, void* stream) {
+  if (tokens < 1 || heads < 1 || in_dim < 16 || in_dim > 1024 || in_dim % 16 != 0 ||
+      out_dim < 32 || out_dim % 32 != 0)
+    return MLA_ERR_INVALID;
+  if ((int64_t)in_dim * out_dim >= ((int64_t)1 << 30)) return MLA_ERR_INVALID;
+  if ((int64_t)tokens * heads * std::max(in_dim, out_dim) >= ((int64_t)1 << 40)) return MLA_ERR_INVALID;
+  if ((int64_t)heads * (out_dim / 32) > 0x7fffffff) return MLA_ERR_INVALID;
+  if (!x || !w || !y || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return MLA_ERR_INVALID;
+  const int rc = check_device();
+  if (rc != MLA_OK) return rc;
+  mlav::ProjArgs a;
+  a.x = x;
+  a.w = w;
+  a.y = y;
+  a.tokens = tokens;
+  a.heads = heads;
+  a.in_dim = in_dim;
+  a.out_dim = out_dim;
+  if (mlav::launch_proj_kernel(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_verify_strerror(int code) {
   switch (code) {
     case MLA_OK: return "success";

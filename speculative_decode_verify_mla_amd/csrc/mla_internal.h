@@ -82,6 +82,15 @@ struct CompactArgs {
 };
 hipError_t launch_compact_kernel(const CompactArgs& a, int batch, hipStream_t stream);
 
+// Per-head projections around absorbed attention (mla_proj.hip).
+struct ProjArgs {
+  const uint16_t* x;  // [tokens, heads, in_dim] bf16
+  const uint16_t* w;  // [heads, in_dim, out_dim] bf16
+  uint16_t* y;        // [tokens, heads, out_dim] bf16
+  int32_t tokens, heads, in_dim, out_dim;
+};
+hipError_t launch_proj_kernel(const ProjArgs& a, hipStream_t stream);
+
 // Launchers (defined in mla_kernels.hip). Return the hipError_t of the launch.
 hipError_t launch_split_kernel(const MainArgs& a, int mode, hipStream_t stream);
 hipError_t launch_combine_kernel(const MainArgs& a, int mode, hipStream_t stream);

@@ -34,19 +34,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mlav {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kLatBytes = kTile * kDL * 2;    // 65536: latent part of a tile
 constexpr int kRopeBytes = kTile * kDR * 2;   // 8192: rope part of a tile
@@ -56,7 +48,6 @@ constexpr int kLdsBytes = kStages * kStageBytes;  // 147456
 static_assert(kLdsBytes + 16 <= 163840, "two KV stages must fit one gfx950 CU's 160 KB LDS");
 constexpr int kLoadsPerStage = kStageBytes / (64 * 16);  // 72 wave-wide 16-byte loads
 static_assert(kLoadsPerStage == 72 && kLoadsPerStage % kWaves == 0, "load split");
-constexpr unsigned kBufferConfig = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr unsigned kOobOffset = 0x80000000u;     // an offset every range check rejects
 constexpr float kOverflowLog2 = 32.0f;           // largest exponent (log2 units) a term may take
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -84,38 +75,6 @@ __device__ __forceinline__ int swz_rope(int key) {  // permutes the 3 chunk bits
   return ((key >> 1) ^ (key << 2)) & 7;
 }
 
-// Generic -> LDS address-space pointers (the arrays live in LDS; the casts only
-// let the compiler emit ds_* / LDS-DMA instructions directly).
-__device__ __forceinline__ bf16x8 lds_read16(const uint8_t* base, unsigned off) {
-  const LDS_AS uint8_t* p = (const LDS_AS uint8_t*)(base) + off;
-  return *(const LDS_AS bf16x8*)p;
-}
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* base, unsigned off) {
-  LDS_AS uint8_t* p = (LDS_AS uint8_t*)(base) + off;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
-}
-
-__device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds_dst,
-                                              unsigned voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(lds_dst), 16, voffset, 0, 0, 0);
-}
-
-// Buffer descriptors are wave-uniform; readfirstlane keeps them in SGPRs even
-// when the compiler cannot prove uniformity (it would otherwise emit a loop).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t v = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
-                                           (int)kBufferConfig);
-}
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 // Score MFMAs with VGPR accumulators. Every accumulating MFMA in a function is
 // otherwise given AGPR accumulators, and the 256 output accumulators already
 // fill the AGPR file; scores are consumed by VALU code, so they belong in VGPRs.
@@ -138,10 +97,6 @@ __device__ __forceinline__ void score_fence(f32x16& s) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ uint16_t bf16_bits(float x) {
-  __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
-  return __builtin_bit_cast(uint16_t, h);
-}
 
 // Keys of one query group and how its tiles are split (shared by both kernels).
 struct GroupInfo {

@@ -1,0 +1,112 @@
+// Per-head projections either side of absorbed MLA attention, on gfx950.
+//
+// Absorbed MLA ("The Shared Memory Ceiling", section "The Broader Context:
+// Building a Custom sm_120 Verify Kernel": attention over the shared MLA
+// latent) needs each head's query in latent space before the verify call and
+// brings each head's latent output back to its value space after it:
+//     q_lat[m, h, :]  = q_nope[m, h, :] . W_UK[h]     (128 -> 512 per head)
+//     o_head[m, h, :] = out_lat[m, h, :] . W_UV[h]    (512 -> 128 per head)
+// Both are y[m, h, :] = x[m, h, :] . W[h] for tokens m, with W[h] row-major
+// [in_dim, out_dim] in bf16, fp32 accumulation and a bf16 (RNE) result.
+//
+// With a verify step's few tokens the product is bound by reading the weights
+// (8.4 MB per projection at 64 heads). One wave owns 32 output columns of one
+// head: it DMAs that weight slice (in_dim rows x 64 B) into LDS once, then for
+// each 32-token tile runs in_dim/16 MFMAs 32x32x16 computing Y^T = W^T X^T:
+// W^T fragments come from the row-major slice through transposing LDS reads
+// (the same access as the attention kernel's V^T operand), X^T fragments are
+// 16-byte loads of 8 consecutive input dims of one token.
+#include <hip/hip_runtime.h>
+
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mlav {
+
+namespace {
+
+constexpr int kProjCols = 32;  // output columns per wave (one MFMA tile)
+constexpr int kXBatch = 16;    // k-steps whose token loads are issued together
+
+__global__ void __launch_bounds__(64) mla_proj_kernel(ProjArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t wslice[];  // in_dim rows x 64 B
+  const int lane = threadIdx.x;
+  const int tiles_n = a.out_dim / kProjCols;
+  const int h = blockIdx.x / tiles_n;
+  const int n0 = (blockIdx.x - h * tiles_n) * kProjCols;
+  const int K = a.in_dim;
+
+  // ---- weight slice W[h, 0:K, n0:n0+32] -> LDS (dense rows of 64 bytes) ----
+  // One DMA instruction moves 16 rows: lane l fetches row 16i + l/4, chunk l%4.
+  {
+    const uint16_t* wbase = a.w + (int64_t)h * K * a.out_dim + n0;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(wbase, (uint32_t)((int64_t)K * a.out_dim * 2));
+    for (int i = 0; i < K / 16; ++i) {
+      const unsigned off = (unsigned)(((16 * i + (lane >> 2)) * a.out_dim) * 2 + (lane & 3) * 16);
+      buffer_to_lds(rs, wslice + i * 1024, off);
+    }
+  }
+
+  // A operand (W^T, rows = output column n, k = input dim): lane l needs column
+  // l%32 at input dims k0 + 8*(l/32) + 0..7. In each 16-lane group G, lane i of a
+  // transposing read addresses row (k) base + i/4, columns 4*(i%4)..+3, and gets
+  // column i of the group's 16 columns for the 4 rows.
+  const int G = lane >> 4, i = lane & 15;
+  const unsigned abase = (unsigned)((8 * (G >> 1) + (i >> 2)) * 64 + (16 * (G & 1) + 4 * (i & 3)) * 2);
+
+  const int M = a.tokens;
+  const int ksteps = K / 16;
+  bool slice_ready = false;
+  for (int m0 = 0; m0 < M; m0 += 32) {
+    // B operand (X^T, k = input dim, column = token m): lane l reads token
+    // m0 + l%32, input dims k0 + 8*(l/32) + 0..7 (16 bytes). Tokens past M reuse
+    // the last token and are not stored.
+    const int m = min(m0 + (lane & 31), M - 1);
+    const uint16_t* xrow = a.x + ((int64_t)m * a.heads + h) * K + 8 * (lane >> 5);
+    f32x16 acc = {};
+    for (int c0 = 0; c0 < ksteps; c0 += kXBatch) {
+      bf16x8 xb[kXBatch];
+#pragma unroll
+      for (int j = 0; j < kXBatch; ++j)
+        if (c0 + j < ksteps) xb[j] = *reinterpret_cast<const bf16x8*>(xrow + 16 * (c0 + j));
+      if (!slice_ready) {
+        // the first token loads are in flight with the weight DMA: one wait for both
+        __builtin_amdgcn_s_waitcnt(0);
+        slice_ready = true;
+      }
+#pragma unroll
+      for (int j = 0; j < kXBatch; ++j) {
+        if (c0 + j < ksteps) {
+          const int k0 = 16 * (c0 + j);
+          const bf16x4 w0 = lds_read_tr(wslice, abase + (unsigned)(k0 * 64));
+          const bf16x4 w1 = lds_read_tr(wslice, abase + (unsigned)((k0 + 4) * 64));
+          const bf16x8 wa = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+          acc = mfma32(wa, xb[j], acc);
+        }
+      }
+    }
+    // C layout: lane l holds token m0 + l%32 and output columns
+    // 8*(r/4) + 4*(l/32) + r%4, r = 0..15: four runs of 4 consecutive columns.
+    if (m0 + (lane & 31) < M) {
+      uint16_t* yrow = a.y + ((int64_t)(m0 + (lane & 31)) * a.heads + h) * a.out_dim + n0 + 4 * (lane >> 5);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 pk;
+        pk.x = (uint32_t)bf16_bits(acc[4 * g + 0]) | ((uint32_t)bf16_bits(acc[4 * g + 1]) << 16);
+        pk.y = (uint32_t)bf16_bits(acc[4 * g + 2]) | ((uint32_t)bf16_bits(acc[4 * g + 3]) << 16);
+        *reinterpret_cast<uint2*>(yrow + 8 * g) = pk;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_proj_kernel(const ProjArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)a.heads * (unsigned)(a.out_dim / kProjCols);
+  const size_t lds = (size_t)a.in_dim * kProjCols * 2;
+  hipLaunchKernelGGL(mla_proj_kernel, dim3(grid), dim3(64), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mlav
