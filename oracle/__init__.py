@@ -11,6 +11,7 @@ Contents:
   compaction  – post-verify KV compaction (accepted draft rows moved to the
                 front of the draft region), the plain definition.
   projection  – per-head projections into and out of the latent space.
+  topk        – top-k index selection (the sparse path's index lists).
 
 Every function is pinned by tests under -m "not gpu" against brute force,
 a textbook attention routine (torch SDPA in float64), closed forms and
@@ -26,3 +27,4 @@ from .definition import (  # noqa: F401
 )
 from .compaction import compact_kv  # noqa: F401
 from .projection import head_project  # noqa: F401
+from .topk import order_key, select_topk  # noqa: F401
