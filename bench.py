@@ -150,9 +150,10 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic plan")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("verify", "compact", "proj"), default="verify",
+    ap.add_argument("--op", choices=("verify", "compact", "proj", "topk"), default="verify",
                     help="verify: the attention call (default); compact: post-verify KV "
-                         "compaction; proj: the per-head projections around it")
+                         "compaction; proj: the per-head projections around it; topk: "
+                         "top-k index selection for the sparse path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (hardware counter scale)")
     args = ap.parse_args()
@@ -189,6 +190,9 @@ def main():
         return
     if args.op == "proj":
         bench_proj(args, dev)
+        return
+    if args.op == "topk":
+        bench_topk(args, dev)
         return
 
     w = synth.config(args.config)
@@ -509,6 +513,56 @@ def bench_proj(args, dev):
                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
                      "kernel": "mla_proj_kernel"},
         "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_topk(args, dev):
+    """Top-k selection over one score per cached position, for every query token
+    of the sparse workload (default config 5: 32 tokens x 131,072, k = 2048)."""
+    import numpy as np
+    import torch
+
+    import speculative_decode_verify_mla_amd as mv
+    from speculative_decode_verify_mla_amd import synth
+
+    cfg = args.config if args.config in (5,) else 5
+    w = synth.config(cfg)
+    R, L, k = w.B * w.T, int(w.kv_seq_stride), int(w.topk)
+    rng = np.random.default_rng(3000 + cfg)
+    copies = [torch.from_numpy(rng.standard_normal((R, L)).astype(np.float32)).to(dev)
+              for _ in range(max(args.copies, 1))]
+    lens = torch.from_numpy(np.repeat(w.kv_lens, w.T).astype(np.int32)).to(dev)
+    out = torch.empty((R, k), dtype=torch.int32, device=dev)
+
+    def call(i, st):
+        mv.select_topk(copies[i % len(copies)], k, out, row_lens=lens, stream=st)
+
+    eager_us, us = _time_small_op(call, args.steps, args.warmup, dev)
+    nbytes = R * L * 4 + R * k * 4 + R * 4
+    gbps = nbytes / (us * 1e-6) / 1e9
+    log(f"top-k: {R} rows x {L}, k={k}: {us:.2f} us (graph), {eager_us:.2f} us eager, {gbps:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        host = copies[0].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.select_topk(host[:4], k, np.repeat(w.kv_lens, w.T)[:4])
+        el = time.perf_counter() - t0
+        cpu = dict(value=el / 4 * R * 1e6, unit="us/call", cores=1, kind="oracle",
+                   sample=f"4 of the {R} rows (numpy lexsort), scaled to the whole call")
+    line = {
+        "metric": "top-k index selection µs/call (sparse decode indices)", "value": round(us, 3),
+        "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded N(0,1) scores)",
+        "config": {"workload": w.spec.name, "rows": R, "candidates": L, "k": k},
+        "eager_us_per_call": round(eager_us, 3), "timing": "graph replay of the timed calls",
+        "algorithmic_bytes": nbytes, "achieved_hbm_GBps": round(gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "mla_topk_kernel"},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -204,6 +204,25 @@ int mla_compact_kv(const mla_dims* dims, uint16_t* c_kv, uint16_t* k_rope,
 int mla_head_project(int32_t tokens, int32_t heads, int32_t in_dim, int32_t out_dim,
                      const uint16_t* x, const uint16_t* w, uint16_t* y, void* stream);
 
+/* Top-k index selection for the sparse path ("The SMEM Ceiling", section "The
+ * Problem Space: Sparse Decode on Blackwell": each decode token attends only to
+ * the top-k set an index-selection step picks). The scores are inputs.
+ *
+ * For each row r (a query token) with n = row_lens[r] clamped to [0, row_len]
+ * candidates (row_len when row_lens is NULL): positions p < n are ranked by
+ * scores[r, p] (IEEE-754 total order of float32: -inf < ... < -0.0 < +0.0 < ...
+ * < +inf, every NaN below every number), ties by lower p; the first min(k, n)
+ * positions are written to indices[r, :] in ascending order and the rest of the
+ * k slots are -1 (which mla_sparse_attn skips).
+ *
+ * scores fp32 [rows, row_stride] (16-byte aligned, row_stride >= row_len and a
+ * multiple of 4: rows are read 16 bytes at a time), row_lens i32 [rows] or
+ * NULL, indices i32 [rows, k] (4-byte aligned device memory). Checks
+ * (MLA_ERR_INVALID): those, rows >= 1, row_len >= 1, 1 <= k <= 2^20, pointers
+ * non-NULL. Enqueued on `stream`; no workspace. */
+int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k,
+                    const float* scores, const int32_t* row_lens, int32_t* indices, void* stream);
+
 /* Static description of an error code (never NULL). */
 const char* mla_verify_strerror(int code);
 

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     head_project,
     load_library,
     plan,
+    select_topk,
     sparse_attn,
     strerror,
     verify_attn,

@@ -33,6 +33,7 @@ EXPORTED = (
     "mla_verify_strerror",
     "mla_compact_kv",
     "mla_head_project",
+    "mla_select_topk",
 )
 
 
@@ -101,6 +102,8 @@ def load_library(path: Optional[str] = None):
         lib.mla_compact_kv.restype = i32
         lib.mla_head_project.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
         lib.mla_head_project.restype = i32
+        lib.mla_select_topk.argtypes = [i32, i32, ctypes.c_int64, i32, vp, vp, vp, vp]
+        lib.mla_select_topk.restype = i32
         lib.mla_verify_strerror.argtypes = [i32]
         lib.mla_verify_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -259,3 +262,19 @@ def head_project(x, w, y, stream=None):
                                          ctypes.c_void_p(stream.cuda_stream))
     if rc != MLA_OK:
         raise MlaError(rc, "mla_head_project")
+
+
+def select_topk(scores, k: int, indices, row_lens=None, row_len: Optional[int] = None, stream=None):
+    """Top-k positions per row of fp32 scores (mla_select_topk), ascending and -1
+    padded into int32 indices [rows, k]. row_len defaults to scores.shape[1]."""
+    import torch
+
+    rows, stride = scores.shape
+    n = int(stride if row_len is None else row_len)
+    if stream is None:
+        stream = torch.cuda.current_stream(scores.device)
+    rc = load_library().mla_select_topk(int(rows), n, int(stride), int(k), _ptr(scores),
+                                        _ptr(row_lens), _ptr(indices),
+                                        ctypes.c_void_p(stream.cuda_stream))
+    if rc != MLA_OK:
+        raise MlaError(rc, "mla_select_topk")

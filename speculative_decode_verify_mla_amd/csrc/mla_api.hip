@@ -311,6 +311,27 @@ int mla_head_project(int32_t tokens, int32_t heads, int32_t in_dim, int32_t out_
   return MLA_OK;
 }
 
+int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k,
+                    const float* scores, const int32_t* row_lens, int32_t* indices, void* stream) {
+  if (rows < 1 || row_len < 1 || row_stride < row_len || k < 1 || k > (1 << 20)) return MLA_ERR_INVALID;
+  if (row_stride % 4 != 0) return MLA_ERR_INVALID;  // rows are read 16 bytes at a time
+  if (!scores || !indices || !aligned(scores, 16) || !aligned(indices, 4) ||
+      (row_lens && !aligned(row_lens, 4)))
+    return MLA_ERR_INVALID;
+  const int rc = check_device();
+  if (rc != MLA_OK) return rc;
+  mlav::TopkArgs a;
+  a.scores = scores;
+  a.row_lens = row_lens;
+  a.indices = indices;
+  a.row_stride = row_stride;
+  a.rows = rows;
+  a.row_len = row_len;
+  a.k = k;
+  if (mlav::launch_topk_kernel(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_verify_strerror(int code) {
   switch (code) {
     case MLA_OK: return "success";

@@ -91,6 +91,16 @@ struct ProjArgs {
 };
 hipError_t launch_proj_kernel(const ProjArgs& a, hipStream_t stream);
 
+// Top-k index selection (mla_topk.hip).
+struct TopkArgs {
+  const float* scores;      // [rows, row_stride] fp32
+  const int32_t* row_lens;  // [rows] candidates per row, or NULL (all row_len)
+  int32_t* indices;         // [rows, k] ascending, -1 padded
+  int64_t row_stride;
+  int32_t rows, row_len, k;
+};
+hipError_t launch_topk_kernel(const TopkArgs& a, hipStream_t stream);
+
 // Launchers (defined in mla_kernels.hip). Return the hipError_t of the launch.
 hipError_t launch_split_kernel(const MainArgs& a, int mode, hipStream_t stream);
 hipError_t launch_combine_kernel(const MainArgs& a, int mode, hipStream_t stream);

@@ -195,3 +195,19 @@ def test_compact_invalid_arguments(lib):
     assert call_c(d, pt=P()) == B.MLA_ERR_INVALID  # page table without a page size
     assert call_c(_dims(batch=2, num_q=65, max_kv_len=132, kv_rows=264, kv_seq_stride=132)) == \
         B.MLA_ERR_INVALID
+
+
+def test_topk_and_projection_invalid_arguments(lib):
+    f = lib.mla_select_topk
+    assert f(0, 100, 100, 8, P(), None, P(), None) == B.MLA_ERR_INVALID       # no rows
+    assert f(2, 100, 99, 8, P(), None, P(), None) == B.MLA_ERR_INVALID        # stride < length
+    assert f(2, 98, 98, 8, P(), None, P(), None) == B.MLA_ERR_INVALID         # stride not 4-aligned
+    assert f(2, 100, 100, 0, P(), None, P(), None) == B.MLA_ERR_INVALID       # k = 0
+    assert f(2, 100, 100, 8, None, None, P(), None) == B.MLA_ERR_INVALID
+    assert f(2, 100, 100, 8, FakePtr(0x10004)(), None, P(), None) == B.MLA_ERR_INVALID  # 16-B
+    g = lib.mla_head_project
+    assert g(4, 2, 24, 64, P(), P(), P(), None) == B.MLA_ERR_INVALID          # in_dim % 16
+    assert g(4, 2, 32, 48, P(), P(), P(), None) == B.MLA_ERR_INVALID          # out_dim % 32
+    assert g(4, 2, 2048, 64, P(), P(), P(), None) == B.MLA_ERR_INVALID        # in_dim > 1024
+    assert g(0, 2, 32, 64, P(), P(), P(), None) == B.MLA_ERR_INVALID
+    assert g(4, 2, 32, 64, MIS(), P(), P(), None) == B.MLA_ERR_INVALID
