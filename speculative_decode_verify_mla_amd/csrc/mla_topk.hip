@@ -14,9 +14,11 @@
 //    prefix over the bins finds the digit where the count of larger keys
 //    reaches k. Keys above the final threshold are all selected; of the keys
 //    equal to it, the lowest positions fill the remaining slots.
-//  * One more pass walks the positions in order, 4,096 at a time, and places
-//    each selected position by a block prefix count, so the output comes out
-//    sorted without a sort.
+//  * The selected positions are then placed in position order: each wave
+//    counts the keys above / equal to the threshold in its contiguous segment,
+//    the segments' totals give each its starting offsets, and each wave walks
+//    its segment again placing elements by wave-local prefix sums, so the
+//    output comes out sorted without a sort.
 // Scores are read 16 bytes per lane with 16 per thread in flight; a row is
 // read four times, after the first pass from L2.
 #include <hip/hip_runtime.h>
@@ -30,11 +32,18 @@ namespace {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kMaxBins = 4096;  // 12-bit digits
+constexpr int kWalkBatch = 8;   // 256-score wave steps whose loads are issued together
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   if (x != x) return 0u;  // NaN ranks below every number
   const uint32_t b = __float_as_uint(x);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
 // Block-wide exclusive prefix of one count per thread; `total` gets the sum.
@@ -137,37 +146,92 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_kernel(TopkArgs a) {
   }
 
   // Every key above the threshold `prefix`, and the first k_rem keys equal to
-  // it, in position order. One block scan per 4,096 scores carries both counts
-  // (keys above in the low 16 bits, keys equal in the high 16 bits).
-  int out_base = 0, eq_seen = 0;
-  for (int base = 0; kk > 0 && base < n; base += kSpan) {
-    const int p = base + 4 * tid;
-    const float4 v = p < n ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
-    const float e[4] = {v.x, v.y, v.z, v.w};
-    bool gt[4], eq[4];
+  // it, in position order. An element x goes to slot G(x) + min(E(x), k_rem),
+  // G and E counting the keys above and equal to the threshold before x. Each
+  // wave owns one contiguous segment of the row: it counts its segment, the
+  // 16 wave totals give every segment's starting G and E, and the wave walks
+  // its segment again placing elements with wave-local prefix sums (no block
+  // barrier inside either walk).
+  if (kk > 0) {
+    const int lane = tid & 63, wave = tid >> 6;
+    const int seg = (n + kTopkWaves * 256 - 1) / (kTopkWaves * 256) * 256;  // whole 256-score steps
+    const int w0 = wave * seg, w1 = min(w0 + seg, n);
     int ngt = 0, neq = 0;
+    for (int base = w0; base < w1; base += kWalkBatch * 256) {
+      float4 v[kWalkBatch];  // the batch's loads are all in flight before any is used
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t u = order_key(e[q]);
-      gt[q] = p + q < n && u > prefix;
-      eq[q] = p + q < n && u == prefix;
-      ngt += gt[q];
-      neq += eq[q];
-    }
-    int tot;
-    const int ex = block_excl_scan(ngt | (neq << 16), wave_tot, tot);
-    int gt_before = ex & 0xffff, eq_before = ex >> 16;
-    const int eq_left = max(k_rem - eq_seen, 0);  // equal keys this step may still take
+      for (int j = 0; j < kWalkBatch; ++j) {
+        const int p = base + 256 * j + 4 * lane;
+        v[j] = p < w1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool take = gt[q] || (eq[q] && eq_before < eq_left);
-      const int pos = out_base + gt_before + min(eq_before, eq_left);
-      if (take && pos < kk) out[pos] = p + q;  // (the counts give exactly kk)
-      gt_before += gt[q];
-      eq_before += eq[q];
+      for (int j = 0; j < kWalkBatch; ++j) {
+        const int p = base + 256 * j + 4 * lane;
+        const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t u = order_key(e[q]);
+          ngt += (p + q < w1 && u > prefix);
+          neq += (p + q < w1 && u == prefix);
+        }
+      }
     }
-    out_base += (tot & 0xffff) + min(tot >> 16, eq_left);
-    eq_seen += tot >> 16;
+    const int wgt = wave_sum_i(ngt), weq = wave_sum_i(neq);
+    __shared__ int seg_gt[kTopkWaves], seg_eq[kTopkWaves];
+    if (lane == 0) {
+      seg_gt[wave] = wgt;
+      seg_eq[wave] = weq;
+    }
+    __syncthreads();
+    int G = 0, E = 0;  // keys above / equal before this wave's segment
+    for (int w = 0; w < wave; ++w) {
+      G += seg_gt[w];
+      E += seg_eq[w];
+    }
+    for (int base = w0; base < w1; base += kWalkBatch * 256) {
+      float4 vb[kWalkBatch];
+#pragma unroll
+      for (int j = 0; j < kWalkBatch; ++j) {
+        const int pj = base + 256 * j + 4 * lane;
+        vb[j] = pj < w1 ? load4(s, pj) : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < kWalkBatch; ++j) {
+      const int p = base + 256 * j + 4 * lane;
+      const float4 v = vb[j];
+      const float e[4] = {v.x, v.y, v.z, v.w};
+      bool gt[4], eq[4];
+      int cg = 0, ce = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t u = order_key(e[q]);
+        gt[q] = p + q < w1 && u > prefix;
+        eq[q] = p + q < w1 && u == prefix;
+        cg += gt[q];
+        ce += eq[q];
+      }
+      // wave-exclusive prefix of (cg, ce), packed as cg | ce << 16
+      const int packed = cg | (ce << 16);
+      int incl = packed;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const int step_tot = __shfl(incl, 63);
+      int g = G + ((incl - packed) & 0xffff), eqb = E + ((incl - packed) >> 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool take = gt[q] || (eq[q] && eqb < k_rem);
+        const int pos = g + min(eqb, k_rem);
+        if (take && pos < kk) out[pos] = p + q;  // (the counts give exactly kk)
+        g += gt[q];
+        eqb += eq[q];
+      }
+      G += step_tot & 0xffff;
+      E += step_tot >> 16;
+      }
+    }
   }
   for (int i = kk + tid; i < k; i += kTopkThreads) out[i] = -1;
 }
