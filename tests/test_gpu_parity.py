@@ -57,6 +57,11 @@ SMALL = [
     Spec("sparse_h32_k70", B=2, T=3, H=32, layout="sparse", cache_len=900, topk=70),
     Spec("sparse_paged", B=2, T=2, H=64, layout="sparse", cache_len=3000, topk=200,
          paged_sparse=True),
+    # groups of at most 32 rows: one wave computes, three only load
+    Spec("paged_t2_h16", B=3, T=2, H=16, layout="paged", prefix=[50, 900, 4100]),
+    Spec("contig_t1_h8", B=2, T=1, H=8, layout="contig", prefix=[129, 3000]),
+    Spec("sparse_paged_h16", B=2, T=2, H=16, layout="sparse", cache_len=2000, topk=150,
+         paged_sparse=True),
 ]
 
 
