@@ -26,7 +26,13 @@ __device__ __forceinline__ bf16x8 lds_read16(const uint8_t* base, unsigned off) 
   return *(const LDS_AS bf16x8*)p;
 }
 
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* base, unsigned off) {
+// Transposing read (ds_read_b64_tr_b16). The intrinsic carries no type-based
+// alias information, and an LDS read without any is made to wait for every
+// buffer->LDS DMA in flight (s_waitcnt vmcnt(0)), the next tile's loads included.
+// The restrict qualifier attaches alias scopes, which lifts that wait, as for
+// the plain typed reads. Callers order DMA writes before reads themselves
+// (s_waitcnt on the loads, then a barrier when other waves issued them).
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* __restrict__ base, unsigned off) {
   LDS_AS uint8_t* p = (LDS_AS uint8_t*)(base) + off;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
 }

@@ -810,18 +810,20 @@ mla_split_kernel(MainArgs a) {
 // w_s = 2^{lq_s} / sum_s' 2^{lq_s'}, where lq_s is split s's log2-sum of the
 // rounded terms its partial was normalised by (an exact convex combination of
 // the accumulated terms) and lse_s the same from fp32 terms.
-// Block = one 32-dim block of one wave record (32 rows x 32 dims). The block
-// first turns the (row, split) statistics into normalised weights in LDS, then
-// each thread issues all its split loads before accumulating.
+// Block = one 32-dim block of one wave record (32 rows x 32 dims). Each thread
+// first issues the loads of up to 32 splits' partials, the block turns the
+// (row, split) statistics into unnormalised weights in LDS meanwhile, and the
+// row's 1 / sum of weights scales the accumulated output once.
 // ---------------------------------------------------------------------------
 static_assert(16 * 256 * 4 == kRecElems, "16 combine blocks of 256 threads x 4 dims cover one wave record");
 
 template <int MODE>
 __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
-  __shared__ float wts[kRowsPerWave][kMaxSplits + 1];  // normalised weight x fp16 scale
+  __shared__ float wts[kRowsPerWave][kMaxSplits + 1];  // unnormalised weight x fp16 scale
   __shared__ float red[3][8][kRowsPerWave];
   __shared__ float row_lse[kRowsPerWave];
+  __shared__ float row_inv[kRowsPerWave];  // 1 / sum of the unnormalised weights
 
   const int bid = blockIdx.x;
   const int db = bid & 15;
@@ -856,22 +858,40 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
   const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
 
-  // The first 16 splits' partials (4 dims of one row per thread) are loaded
-  // before the weights are formed, so the two memory round trips overlap.
+  // The first kBatch splits' partials (4 dims of one row per thread) are
+  // loaded before the weights are formed, so the two memory round trips overlap
+  // (and with at most kBatch splits there is no other).
+  constexpr int kBatch = 32;
   const int lane = t & 63, qq = t >> 6, half = lane >> 5, l32 = lane & 31;
   const uint16_t* o_p = a.ws_o + rec0 * kRecElems + ((db * 4 + qq) * 64 + lane) * 4;
   const int64_t o_step = rec_stride * kRecElems;
-  uint2 raw[16];
+  uint2 raw[kBatch];
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < kBatch; ++j)
     raw[j] = j < n_active ? *reinterpret_cast<const uint2*>(o_p + j * o_step) : uint2{0u, 0u};
 
   // ---- phase 1: per-row maxima, sums and weights (thread = row x split lane) ----
   {
     const int r = t & 31, sl = t >> 5;  // 8 split lanes per row
     const float* st = a.ws_lse + rec0 * (kRecRowStats * kRowsPerWave) + r;
+    // the statistics of the first kBatch splits stay in registers (one load each)
+    constexpr int kHeld = kBatch / 8;
+    float h_le[kHeld], h_lq[kHeld], h_sc[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      const int s = sl + 8 * i;
+      const bool v = s < n_active;
+      h_le[i] = v ? st[s * st_step] : -__builtin_inff();
+      h_lq[i] = v ? st[s * st_step + kRowsPerWave] : -__builtin_inff();
+      h_sc[i] = v ? st[s * st_step + 2 * kRowsPerWave] : 0.f;
+    }
     float mx = -__builtin_inff(), mxq = -__builtin_inff();
-    for (int s = sl; s < n_active; s += 8) {
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      mx = fmaxf(mx, h_le[i]);
+      mxq = fmaxf(mxq, h_lq[i]);
+    }
+    for (int s = sl + kBatch; s < n_active; s += 8) {
       mx = fmaxf(mx, st[s * st_step]);
       mxq = fmaxf(mxq, st[s * st_step + kRowsPerWave]);
     }
@@ -885,7 +905,17 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
     }
     __syncthreads();
     float es = 0.f, ws = 0.f;
-    for (int s = sl; s < n_active; s += 8) {
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      const int s = sl + 8 * i;
+      if (s < n_active) {
+        const float w = h_lq[i] == -__builtin_inff() ? 0.f : fast_exp2(h_lq[i] - mxq);
+        es += h_le[i] == -__builtin_inff() ? 0.f : fast_exp2(h_le[i] - mx);
+        ws += w;
+        wts[r][s] = w * h_sc[i];
+      }
+    }
+    for (int s = sl + kBatch; s < n_active; s += 8) {
       const float le = st[s * st_step], lq = st[s * st_step + kRowsPerWave];
       const float w = lq == -__builtin_inff() ? 0.f : fast_exp2(lq - mxq);
       es += le == -__builtin_inff() ? 0.f : fast_exp2(le - mx);
@@ -902,8 +932,7 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
       es += red[0][j][r];
       ws += red[1][j][r];
     }
-    const float inv = ws > 0.f ? 1.0f / ws : 0.f;
-    for (int s = sl; s < n_active; s += 8) wts[r][s] *= inv;
+    if (sl == 0) row_inv[r] = ws > 0.f ? 1.0f / ws : 0.f;
     if (sl == 0)
       row_lse[r] = (mx != -__builtin_inff() && es > 0.f) ? (mx + fast_log2(es)) * kLn2 : -__builtin_inff();
     __syncthreads();
@@ -912,14 +941,14 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   // ---- phase 2: out = sum_s w_s o_s for 4 dims per thread -------------------------
   const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < n_active; s0 += 16) {
+  for (int s0 = 0; s0 < n_active; s0 += kBatch) {
     if (s0 > 0) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < kBatch; ++j)
         raw[j] = s0 + j < n_active ? *reinterpret_cast<const uint2*>(o_p + (s0 + j) * o_step) : uint2{0u, 0u};
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kBatch; ++j) {
       if (s0 + j < n_active) {
         const float w = wts[l32][s0 + j];
         acc[0] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].x & 0xffffu));
@@ -930,6 +959,11 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
     }
   }
   if (row >= a.rows_per_group) return;
+  const float inv = row_inv[l32];
+  acc[0] *= inv;
+  acc[1] *= inv;
+  acc[2] *= inv;
+  acc[3] *= inv;
   const int64_t qrow = (int64_t)group * a.rows_per_group + row;
   const int d = db * 32 + 8 * qq + 4 * half;
   uint2 pkd;
