@@ -967,8 +967,8 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   const int64_t qrow = (int64_t)group * a.rows_per_group + row;
   const int d = db * 32 + 8 * qq + 4 * half;
   uint2 pkd;
-  pkd.x = (uint32_t)bf16_bits(acc[0]) | ((uint32_t)bf16_bits(acc[1]) << 16);
-  pkd.y = (uint32_t)bf16_bits(acc[2]) | ((uint32_t)bf16_bits(acc[3]) << 16);
+  pkd.x = pack_bf16x2(acc[0], acc[1]);
+  pkd.y = pack_bf16x2(acc[2], acc[3]);
   *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
   if (db == 0 && qq == 0 && half == 0) a.lse[qrow] = row_lse[l32];
 }

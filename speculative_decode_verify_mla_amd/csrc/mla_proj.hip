@@ -92,8 +92,8 @@ __global__ void __launch_bounds__(64) mla_proj_kernel(ProjArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 pk;
-        pk.x = (uint32_t)bf16_bits(acc[4 * g + 0]) | ((uint32_t)bf16_bits(acc[4 * g + 1]) << 16);
-        pk.y = (uint32_t)bf16_bits(acc[4 * g + 2]) | ((uint32_t)bf16_bits(acc[4 * g + 3]) << 16);
+        pk.x = pack_bf16x2(acc[4 * g + 0], acc[4 * g + 1]);
+        pk.y = pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3]);
         *reinterpret_cast<uint2*>(yrow + 8 * g) = pk;
       }
     }
