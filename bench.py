@@ -538,10 +538,16 @@ def bench_topk(args, dev):
     def call(i, st):
         mv.select_topk(copies[i % len(copies)], k, out, row_lens=lens, stream=st)
 
+    def call_one_wg(i, st):
+        mv.select_topk(copies[i % len(copies)], k, out, row_lens=lens, split_rows=False, stream=st)
+
+    pieces_ws = mv.topk_workspace_bytes(R, L)
     eager_us, us = _time_small_op(call, args.steps, args.warmup, dev)
+    _, one_wg_us = _time_small_op(call_one_wg, args.steps, args.warmup, dev)
     nbytes = R * L * 4 + R * k * 4 + R * 4
     gbps = nbytes / (us * 1e-6) / 1e9
-    log(f"top-k: {R} rows x {L}, k={k}: {us:.2f} us (graph), {eager_us:.2f} us eager, {gbps:.0f} GB/s")
+    log(f"top-k: {R} rows x {L}, k={k}: {us:.2f} us (graph), {eager_us:.2f} us eager, {gbps:.0f} GB/s; "
+        f"one workgroup per row: {one_wg_us:.2f} us (graph)")
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -558,10 +564,11 @@ def bench_topk(args, dev):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded N(0,1) scores)",
         "config": {"workload": w.spec.name, "rows": R, "candidates": L, "k": k},
         "eager_us_per_call": round(eager_us, 3), "timing": "graph replay of the timed calls",
+        "one_workgroup_per_row_us": round(one_wg_us, 3), "workspace_bytes": int(pieces_ws),
         "algorithmic_bytes": nbytes, "achieved_hbm_GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "mla_topk_kernel"},
+                     "kernel": "mla_topk_level_kernel x4 + mla_topk_place_kernel (whole call)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -219,9 +219,23 @@ int mla_head_project(int32_t tokens, int32_t heads, int32_t in_dim, int32_t out_
  * multiple of 4: rows are read 16 bytes at a time), row_lens i32 [rows] or
  * NULL, indices i32 [rows, k] (4-byte aligned device memory). Checks
  * (MLA_ERR_INVALID): those, rows >= 1, row_len >= 1, 1 <= k <= 2^20, pointers
- * non-NULL. Enqueued on `stream`; no workspace. */
+ * non-NULL, workspace 16-byte aligned when given.
+ *
+ * workspace: NULL runs one workgroup per row (no scratch memory). With a
+ * device buffer of at least mla_select_topk_workspace_bytes(rows, row_len)
+ * bytes, rows are spread over several workgroups when there are too few rows
+ * to fill the GPU (five kernel launches; the buffer holds per-piece digit
+ * histograms and is fully rewritten by every call, so it needs no clearing).
+ * A smaller non-NULL buffer than that path needs is MLA_ERR_WORKSPACE. The
+ * result is identical either way. Calls sharing one workspace must be ordered
+ * on one stream. Enqueued on `stream`. */
 int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k,
-                    const float* scores, const int32_t* row_lens, int32_t* indices, void* stream);
+                    const float* scores, const int32_t* row_lens, int32_t* indices,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for mla_select_topk's several-workgroup path on any device
+ * (0 when rows are never split: row_len <= 4096 or invalid arguments). */
+size_t mla_select_topk_workspace_bytes(int32_t rows, int32_t row_len);
 
 /* Static description of an error code (never NULL). */
 const char* mla_verify_strerror(int code);

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     load_library,
     plan,
     select_topk,
+    topk_workspace_bytes,
     sparse_attn,
     strerror,
     verify_attn,

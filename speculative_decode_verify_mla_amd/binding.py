@@ -34,6 +34,7 @@ EXPORTED = (
     "mla_compact_kv",
     "mla_head_project",
     "mla_select_topk",
+    "mla_select_topk_workspace_bytes",
 )
 
 
@@ -102,8 +103,10 @@ def load_library(path: Optional[str] = None):
         lib.mla_compact_kv.restype = i32
         lib.mla_head_project.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
         lib.mla_head_project.restype = i32
-        lib.mla_select_topk.argtypes = [i32, i32, ctypes.c_int64, i32, vp, vp, vp, vp]
+        lib.mla_select_topk.argtypes = [i32, i32, ctypes.c_int64, i32, vp, vp, vp, vp, sz, vp]
         lib.mla_select_topk.restype = i32
+        lib.mla_select_topk_workspace_bytes.argtypes = [i32, i32]
+        lib.mla_select_topk_workspace_bytes.restype = sz
         lib.mla_verify_strerror.argtypes = [i32]
         lib.mla_verify_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -147,12 +150,14 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _workspace(device, nbytes: int):
+def _workspace(device, nbytes: int, tag: str = "attn"):
+    """A cached device buffer of at least nbytes per (device, tag). Calls that use
+    the same cached buffer must be ordered on one stream."""
     import torch
 
     if nbytes == 0:
         return None
-    key = (device.type, device.index)
+    key = (device.type, device.index, tag)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -264,17 +269,31 @@ def head_project(x, w, y, stream=None):
         raise MlaError(rc, "mla_head_project")
 
 
-def select_topk(scores, k: int, indices, row_lens=None, row_len: Optional[int] = None, stream=None):
+def topk_workspace_bytes(rows: int, row_len: int) -> int:
+    return int(load_library().mla_select_topk_workspace_bytes(int(rows), int(row_len)))
+
+
+def select_topk(scores, k: int, indices, row_lens=None, row_len: Optional[int] = None,
+                workspace=None, split_rows: bool = True, stream=None):
     """Top-k positions per row of fp32 scores (mla_select_topk), ascending and -1
-    padded into int32 indices [rows, k]. row_len defaults to scores.shape[1]."""
+    padded into int32 indices [rows, k]. row_len defaults to scores.shape[1].
+    split_rows=False passes no workspace (one workgroup per row); otherwise the
+    given workspace, or a cached one of mla_select_topk_workspace_bytes, lets
+    the library spread short batches of rows over several workgroups."""
     import torch
 
     rows, stride = scores.shape
     n = int(stride if row_len is None else row_len)
     if stream is None:
         stream = torch.cuda.current_stream(scores.device)
+    if not split_rows:
+        workspace = None
+    elif workspace is None:
+        workspace = _workspace(scores.device, topk_workspace_bytes(rows, n), tag="topk")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load_library().mla_select_topk(int(rows), n, int(stride), int(k), _ptr(scores),
-                                        _ptr(row_lens), _ptr(indices),
+                                        _ptr(row_lens), _ptr(indices), _ptr(workspace),
+                                        ctypes.c_size_t(ws_bytes),
                                         ctypes.c_void_p(stream.cuda_stream))
     if rc != MLA_OK:
         raise MlaError(rc, "mla_select_topk")

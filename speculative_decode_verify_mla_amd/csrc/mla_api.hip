@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -67,6 +68,22 @@ int device_cus() {
     return 256;
   g_cu_count[dev].store(v, std::memory_order_relaxed);
   return v;
+}
+
+// Pieces per row for top-k selection: enough (row, piece) workgroups for about
+// two per CU, at most kTopkMaxChunks pieces of at least kTopkMinChunk scores,
+// each a whole number of 1024-score steps (`chunk`, if non-NULL). 1 = one
+// workgroup per row. Rows longer than 2^30 keep one workgroup (piece offsets
+// stay far from the 32-bit limit).
+int topk_pieces(int64_t rows, int64_t row_len, int cus, int* chunk) {
+  if (row_len > (int64_t(1) << 30)) return 1;
+  int64_t s = ceil_div(2 * (int64_t)cus, rows);
+  s = std::min<int64_t>(s, mlav::kTopkMaxChunks);
+  s = std::min<int64_t>(s, ceil_div(row_len, mlav::kTopkMinChunk));
+  s = std::max<int64_t>(s, 1);
+  const int64_t c = ceil_div(ceil_div(row_len, s), 1024) * 1024;
+  if (chunk) *chunk = (int)c;
+  return (int)ceil_div(row_len, c);
 }
 
 // MLA_OK on gfx950, MLA_ERR_UNSUPPORTED elsewhere, MLA_ERR_HIP if the runtime fails.
@@ -311,13 +328,24 @@ int mla_head_project(int32_t tokens, int32_t heads, int32_t in_dim, int32_t out_
   return MLA_OK;
 }
 
+size_t mla_select_topk_workspace_bytes(int32_t rows, int32_t row_len) {
+  if (rows < 1 || row_len < 1) return 0;
+  const int pieces = topk_pieces(rows, row_len, INT32_MAX / 4, nullptr);
+  return pieces > 1 ? (size_t)mlav::topk_workspace_bytes(rows, pieces) : 0;
+}
+
 int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k,
-                    const float* scores, const int32_t* row_lens, int32_t* indices, void* stream) {
+                    const float* scores, const int32_t* row_lens, int32_t* indices,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 1 || row_len < 1 || row_stride < row_len || k < 1 || k > (1 << 20)) return MLA_ERR_INVALID;
   if (row_stride % 4 != 0) return MLA_ERR_INVALID;  // rows are read 16 bytes at a time
   if (!scores || !indices || !aligned(scores, 16) || !aligned(indices, 4) ||
-      (row_lens && !aligned(row_lens, 4)))
+      (row_lens && !aligned(row_lens, 4)) || (workspace && !aligned(workspace, 16)))
     return MLA_ERR_INVALID;
+  int chunk = row_len;
+  const int pieces = workspace ? topk_pieces(rows, row_len, device_cus(), &chunk) : 1;
+  if (pieces > 1 && workspace_bytes < (size_t)mlav::topk_workspace_bytes(rows, pieces))
+    return MLA_ERR_WORKSPACE;
   const int rc = check_device();
   if (rc != MLA_OK) return rc;
   mlav::TopkArgs a;
@@ -328,6 +356,9 @@ int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k
   a.rows = rows;
   a.row_len = row_len;
   a.k = k;
+  a.chunks = pieces;
+  a.chunk = pieces > 1 ? chunk : row_len;
+  a.ws = pieces > 1 ? workspace : nullptr;
   if (mlav::launch_topk_kernel(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

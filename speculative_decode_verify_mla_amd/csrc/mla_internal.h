@@ -98,7 +98,20 @@ struct TopkArgs {
   int32_t* indices;         // [rows, k] ascending, -1 padded
   int64_t row_stride;
   int32_t rows, row_len, k;
+  // Several workgroups per row (chunks > 1): the row is cut into `chunks`
+  // pieces of `chunk` scores; the workspace holds the per-piece digit
+  // histograms and the per-row selection state.
+  int32_t chunks, chunk;
+  void* ws;
 };
+constexpr int kTopkMaxChunks = 32;   // pieces per row
+constexpr int kTopkMinChunk = 4096;  // scores per piece, at least
+constexpr int kTopkLevels = 4;       // 8-bit digits of the 32-bit order key
+// Workspace bytes of the several-workgroup path for `rows` rows and `chunks` pieces.
+constexpr int64_t topk_workspace_bytes(int64_t rows, int64_t chunks) {
+  return (int64_t)kTopkLevels * rows * chunks * 256 * 4 + rows * kTopkLevels * 16 +
+         (int64_t)(kTopkLevels - 1) * rows * chunks * 4;
+}
 hipError_t launch_topk_kernel(const TopkArgs& a, hipStream_t stream);
 
 // Launchers (defined in mla_kernels.hip). Return the hipError_t of the launch.

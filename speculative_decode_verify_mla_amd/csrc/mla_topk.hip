@@ -236,10 +236,319 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_kernel(TopkArgs a) {
   for (int i = kk + tid; i < k; i += kTopkThreads) out[i] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Several workgroups per row. With few rows, one workgroup per row leaves most
+// CUs idle, so each row is cut into `chunks` pieces, one 256-thread workgroup
+// per (row, piece), and the radix select runs over 8-bit digits in four
+// launches, most significant digit first. Launch L:
+//  * every workgroup of a row first settles digit L-1: it sums the pieces'
+//    level L-1 histograms (256 bins x pieces) and finds the bin where the count
+//    of larger keys reaches the number still to take (all workgroups of the
+//    row reach the same answer; piece 0 records the new state for launch L+1)
+//    and records its own count of keys in the bins above the settled digit;
+//  * then it histograms digit L of its piece's keys that match the digits
+//    fixed so far and stores the 256 counts (no atomics outside LDS, no
+//    clearing: every piece writes all of its bins).
+// A fifth launch settles the last digit, which gives the threshold key T and
+// how many keys equal to T are taken. A piece's count of keys above T is the
+// sum over levels of its keys above that level's digit, and its count of keys
+// equal to T is its last-level bin of T, so the pieces before it give each
+// piece its output offsets. The piece then places its selected positions in
+// position order as the one-workgroup kernel does.
+// ---------------------------------------------------------------------------
+constexpr int kMwThreads = 256;
+constexpr int kMwWaves = kMwThreads / 64;
+
+struct MwState {
+  uint32_t prefix, pmask;  // digits fixed so far, and their bits
+  int32_t k_rem, pad;      // keys still to take among those matching prefix
+};
+
+__device__ __forceinline__ uint32_t* mw_hist(const TopkArgs& a, int level, int row, int piece) {
+  return reinterpret_cast<uint32_t*>(a.ws) +
+         (((int64_t)level * a.rows + row) * a.chunks + piece) * 256;
+}
+__device__ __forceinline__ MwState* mw_state(const TopkArgs& a, int row, int level) {
+  uint8_t* base = reinterpret_cast<uint8_t*>(a.ws) + (int64_t)kTopkLevels * a.rows * a.chunks * 256 * 4;
+  return reinterpret_cast<MwState*>(base) + (int64_t)row * kTopkLevels + level;
+}
+// Keys of a piece whose digit `level` (< kTopkLevels - 1) is above the settled
+// one (they match the digits above it): written by launch level + 1.
+__device__ __forceinline__ int* mw_above(const TopkArgs& a, int level, int row, int piece) {
+  uint8_t* base = reinterpret_cast<uint8_t*>(a.ws) + (int64_t)kTopkLevels * a.rows * a.chunks * 256 * 4 +
+                  (int64_t)a.rows * kTopkLevels * 16;
+  return reinterpret_cast<int*>(base) + ((int64_t)level * a.rows + row) * a.chunks + piece;
+}
+
+// Block-wide exclusive prefix over the 256 threads (one count each).
+__device__ int mw_excl_scan(int v, int* wave_tot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  int below = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kMwWaves; ++w) {
+    const int t = wave_tot[w];
+    below += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return below + x - v;
+}
+
+// Settles digit `level` of a row from the pieces' level histograms: returns
+// the digit; `taken_above` gets the count of matching keys in higher bins.
+// Every thread of the block must call it; requires k_rem >= 1.
+__device__ uint32_t mw_settle(const TopkArgs& a, int row, int level, int k_rem, int* wave_tot,
+                              uint32_t* s_digit, int* s_above, int& taken_above) {
+  const int tid = threadIdx.x;
+  uint32_t v[kTopkMaxChunks];  // every piece's count of this bin, all loads in flight
+#pragma unroll
+  for (int i = 0; i < kTopkMaxChunks; ++i) v[i] = i < a.chunks ? mw_hist(a, level, row, i)[tid] : 0u;
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkMaxChunks; ++i) c += (int)v[i];
+  int total;
+  const int excl = mw_excl_scan(c, wave_tot, total);
+  const int above = total - excl - c;  // matching keys in bins above this thread's
+  if (above < k_rem && k_rem <= above + c) {  // exactly one bin of the block
+    *s_digit = (uint32_t)tid;
+    *s_above = above;
+  }
+  __syncthreads();
+  const uint32_t d = *s_digit;
+  taken_above = *s_above;
+  __syncthreads();
+  return d;
+}
+
+__device__ __forceinline__ int mw_row_len(const TopkArgs& a, int row) {
+  int n = a.row_lens != nullptr ? a.row_lens[row] : a.row_len;
+  return n < 0 ? 0 : (n > a.row_len ? a.row_len : n);
+}
+
+// Histogram copies in LDS for the first digit: lanes add to copy lane % 16 (at
+// most 4 lanes of a wave instruction per address when keys share a bin, as the
+// top digits of real scores do), 257-word stride so one bin's copies sit in 16
+// different banks. Later digits only count the few keys matching the digits
+// fixed so far and use one copy.
+constexpr int kHistCopies = 16;
+constexpr int kHistStride = 257;
+
+__global__ void __launch_bounds__(kMwThreads) mla_topk_level_kernel(TopkArgs a, int level) {
+  __shared__ uint32_t hist[kHistCopies * kHistStride];
+  __shared__ int wave_tot[kMwWaves];
+  __shared__ uint32_t s_digit;
+  __shared__ int s_above;
+  const int row = blockIdx.x / a.chunks, piece = blockIdx.x - row * a.chunks;
+  const int tid = threadIdx.x;
+  const int n = mw_row_len(a, row);
+  const int kk = min(a.k, n);
+
+  MwState st{0u, 0u, kk, 0};
+  if (level > 0) {
+    st = *mw_state(a, row, level - 1);
+    if (kk > 0) {
+      const int shift = 24 - 8 * (level - 1);
+      int taken;
+      const uint32_t d = mw_settle(a, row, level - 1, st.k_rem, wave_tot, &s_digit, &s_above, taken);
+      st.prefix |= d << shift;
+      st.pmask |= 0xffu << shift;
+      st.k_rem -= taken;
+      // this piece's keys above the settled digit (block sum over the bins above d)
+      const int mine = (uint32_t)tid > d ? (int)mw_hist(a, level - 1, row, piece)[tid] : 0;
+      int piece_above;
+      mw_excl_scan(mine, wave_tot, piece_above);
+      if (tid == 0) *mw_above(a, level - 1, row, piece) = piece_above;
+    } else if (tid == 0) {
+      *mw_above(a, level - 1, row, piece) = 0;
+    }
+  }
+  if (piece == 0 && tid == 0) *mw_state(a, row, level) = st;
+
+  const int copies = level == 0 ? kHistCopies : 1;
+  for (int i = tid; i < copies * kHistStride; i += kMwThreads) hist[i] = 0u;
+  __syncthreads();
+  const int shift = 24 - 8 * level;
+  uint32_t* const my_hist = hist + (tid & (copies - 1)) * kHistStride;
+  const int p0 = piece * a.chunk, p1 = min(p0 + a.chunk, n);
+  const float* s = a.scores + (int64_t)row * a.row_stride;
+  constexpr int kSpan = 4 * kMwThreads;
+  constexpr int kBatch = 8;  // 8 x 16 bytes per thread in flight
+  if (kk > 0) {
+    for (int base = p0; base < p1; base += kBatch * kSpan) {
+      float4 v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int p = base + j * kSpan + 4 * tid;
+        v[j] = p < p1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int p = base + j * kSpan + 4 * tid;
+        const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t u = order_key(e[q]);
+          if (p + q < p1 && (u & st.pmask) == st.prefix) atomicAdd(&my_hist[(u >> shift) & 0xffu], 1u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t c = 0u;
+  for (int i = 0; i < copies; ++i) c += hist[i * kHistStride + tid];
+  mw_hist(a, level, row, piece)[tid] = c;
+}
+
+__global__ void __launch_bounds__(kMwThreads) mla_topk_place_kernel(TopkArgs a) {
+  __shared__ int wave_tot[kMwWaves];
+  __shared__ uint32_t s_digit;
+  __shared__ int s_above;
+  __shared__ int seg_gt[kMwWaves], seg_eq[kMwWaves];
+  const int row = blockIdx.x / a.chunks, piece = blockIdx.x - row * a.chunks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = mw_row_len(a, row);
+  const int kk = min(a.k, n);
+  int32_t* out = a.indices + (int64_t)row * a.k;
+
+  if (kk > 0) {
+    MwState st = *mw_state(a, row, kTopkLevels - 1);
+    int taken;
+    const uint32_t d = mw_settle(a, row, kTopkLevels - 1, st.k_rem, wave_tot, &s_digit, &s_above, taken);
+    const uint32_t T = st.prefix | d;  // the threshold key
+    const int k_eq = st.k_rem - taken;  // keys equal to T that are taken
+
+    // keys above / equal to T in the pieces before this one
+    // Earlier levels: the recorded per-piece counts (thread i < pieces, level
+    // i / pieces); last level: bin counts of the pieces before this one.
+    int g_part = 0, e_part = 0;
+    for (int t = tid; t < (kTopkLevels - 1) * a.chunks; t += kMwThreads) {
+      const int lv = t / a.chunks, i = t - lv * a.chunks;
+      if (i < piece) g_part += *mw_above(a, lv, row, i);
+    }
+    {
+      const bool above = (uint32_t)tid > d, at = (uint32_t)tid == d;
+      uint32_t v[kTopkMaxChunks];  // pieces before this one, all loads in flight
+#pragma unroll
+      for (int i = 0; i < kTopkMaxChunks; ++i)
+        v[i] = (i < piece && (above || at)) ? mw_hist(a, kTopkLevels - 1, row, i)[tid] : 0u;
+#pragma unroll
+      for (int i = 0; i < kTopkMaxChunks; ++i) {
+        g_part += above ? (int)v[i] : 0;
+        e_part += at ? (int)v[i] : 0;
+      }
+    }
+    int G0, E0;
+    mw_excl_scan(g_part, wave_tot, G0);
+    mw_excl_scan(e_part, wave_tot, E0);
+
+    // Each wave owns one contiguous segment of the piece (whole 256-score steps):
+    // count, exchange the wave totals, then walk again placing positions.
+    const float* s = a.scores + (int64_t)row * a.row_stride;
+    const int p0 = piece * a.chunk, p1 = min(p0 + a.chunk, n);
+    const int len = max(p1 - p0, 0);
+    const int seg = (len + kMwWaves * 256 - 1) / (kMwWaves * 256) * 256;
+    const int w0 = p0 + wave * seg, w1 = min(w0 + seg, p1);
+    int ngt = 0, neq = 0;
+    for (int base = w0; base < w1; base += kWalkBatch * 256) {
+      float4 v[kWalkBatch];
+#pragma unroll
+      for (int j = 0; j < kWalkBatch; ++j) {
+        const int p = base + 256 * j + 4 * lane;
+        v[j] = p < w1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < kWalkBatch; ++j) {
+        const int p = base + 256 * j + 4 * lane;
+        const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t u = order_key(e[q]);
+          ngt += (p + q < w1 && u > T);
+          neq += (p + q < w1 && u == T);
+        }
+      }
+    }
+    const int wgt = wave_sum_i(ngt), weq = wave_sum_i(neq);
+    if (lane == 0) {
+      seg_gt[wave] = wgt;
+      seg_eq[wave] = weq;
+    }
+    __syncthreads();
+    int G = G0, E = E0;
+    for (int w = 0; w < wave; ++w) {
+      G += seg_gt[w];
+      E += seg_eq[w];
+    }
+    for (int base = w0; base < w1; base += kWalkBatch * 256) {
+      float4 vb[kWalkBatch];
+#pragma unroll
+      for (int j = 0; j < kWalkBatch; ++j) {
+        const int p = base + 256 * j + 4 * lane;
+        vb[j] = p < w1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < kWalkBatch; ++j) {
+        const int p = base + 256 * j + 4 * lane;
+        const float e[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+        bool gt[4], eq[4];
+        int cg = 0, ce = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t u = order_key(e[q]);
+          gt[q] = p + q < w1 && u > T;
+          eq[q] = p + q < w1 && u == T;
+          cg += gt[q];
+          ce += eq[q];
+        }
+        const int packed = cg | (ce << 16);
+        int incl = packed;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o);
+          if (lane >= o) incl += y;
+        }
+        const int step_tot = __shfl(incl, 63);
+        int g = G + ((incl - packed) & 0xffff), eqb = E + ((incl - packed) >> 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool take = gt[q] || (eq[q] && eqb < k_eq);
+          const int pos = g + min(eqb, k_eq);
+          if (take && pos < kk) out[pos] = p + q;
+          g += gt[q];
+          eqb += eq[q];
+        }
+        G += step_tot & 0xffff;
+        E += step_tot >> 16;
+      }
+    }
+  }
+  if (piece == 0)
+    for (int i = kk + tid; i < a.k; i += kMwThreads) out[i] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_topk_kernel(const TopkArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_topk_kernel, dim3(a.rows), dim3(kTopkThreads), 0, stream, a);
+  if (a.chunks <= 1) {
+    hipLaunchKernelGGL(mla_topk_kernel, dim3(a.rows), dim3(kTopkThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  const unsigned grid = (unsigned)a.rows * (unsigned)a.chunks;
+  for (int level = 0; level < kTopkLevels; ++level) {
+    hipLaunchKernelGGL(mla_topk_level_kernel, dim3(grid), dim3(kMwThreads), 0, stream, a, level);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(mla_topk_place_kernel, dim3(grid), dim3(kMwThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -199,15 +199,28 @@ def test_compact_invalid_arguments(lib):
 
 def test_topk_and_projection_invalid_arguments(lib):
     f = lib.mla_select_topk
-    assert f(0, 100, 100, 8, P(), None, P(), None) == B.MLA_ERR_INVALID       # no rows
-    assert f(2, 100, 99, 8, P(), None, P(), None) == B.MLA_ERR_INVALID        # stride < length
-    assert f(2, 98, 98, 8, P(), None, P(), None) == B.MLA_ERR_INVALID         # stride not 4-aligned
-    assert f(2, 100, 100, 0, P(), None, P(), None) == B.MLA_ERR_INVALID       # k = 0
-    assert f(2, 100, 100, 8, None, None, P(), None) == B.MLA_ERR_INVALID
-    assert f(2, 100, 100, 8, FakePtr(0x10004)(), None, P(), None) == B.MLA_ERR_INVALID  # 16-B
+    assert f(0, 100, 100, 8, P(), None, P(), None, 0, None) == B.MLA_ERR_INVALID   # no rows
+    assert f(2, 100, 99, 8, P(), None, P(), None, 0, None) == B.MLA_ERR_INVALID    # stride < length
+    assert f(2, 98, 98, 8, P(), None, P(), None, 0, None) == B.MLA_ERR_INVALID     # stride % 4
+    assert f(2, 100, 100, 0, P(), None, P(), None, 0, None) == B.MLA_ERR_INVALID   # k = 0
+    assert f(2, 100, 100, 8, None, None, P(), None, 0, None) == B.MLA_ERR_INVALID
+    assert f(2, 100, 100, 8, FakePtr(0x10004)(), None, P(), None, 0, None) == B.MLA_ERR_INVALID
+    assert f(2, 100000, 100000, 8, P(), None, P(), MIS(), 1 << 30, None) == B.MLA_ERR_INVALID
+    # rows long enough to be split over workgroups need the whole workspace
+    assert f(2, 100000, 100000, 8, P(), None, P(), P(), 16, None) == B.MLA_ERR_WORKSPACE
     g = lib.mla_head_project
     assert g(4, 2, 24, 64, P(), P(), P(), None) == B.MLA_ERR_INVALID          # in_dim % 16
     assert g(4, 2, 32, 48, P(), P(), P(), None) == B.MLA_ERR_INVALID          # out_dim % 32
     assert g(4, 2, 2048, 64, P(), P(), P(), None) == B.MLA_ERR_INVALID        # in_dim > 1024
     assert g(0, 2, 32, 64, P(), P(), P(), None) == B.MLA_ERR_INVALID
     assert g(4, 2, 32, 64, MIS(), P(), P(), None) == B.MLA_ERR_INVALID
+
+
+def test_topk_workspace_bytes(lib):
+    w = lib.mla_select_topk_workspace_bytes
+    # 32 pieces of 4096 scores: 4 levels x 32 rows x 32 pieces x 256 bins x 4 B, the
+    # per-row state (4 x 16 B) and 3 levels of per-piece counts (4 B)
+    assert w(32, 131072) == 4 * 32 * 32 * 1024 + 32 * 4 * 16 + 3 * 32 * 32 * 4
+    assert w(1, 4096) == 0          # one piece: no workspace
+    assert w(3, 9000) == 4 * 3 * 3 * 1024 + 3 * 4 * 16 + 3 * 3 * 3 * 4
+    assert w(0, 100) == 0 and w(2, 0) == 0

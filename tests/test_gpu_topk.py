@@ -11,7 +11,7 @@ import speculative_decode_verify_mla_amd as mv
 pytestmark = pytest.mark.gpu
 
 
-def _run(scores, k, row_lens=None, row_len=None):
+def _run(scores, k, row_lens=None, row_len=None, split_rows=True):
     d = torch.device("cuda:0")
     R, L = scores.shape
     if L % 4:  # the call reads rows 16 bytes at a time: pad the stride, keep the length
@@ -20,7 +20,7 @@ def _run(scores, k, row_lens=None, row_len=None):
     s = torch.from_numpy(np.ascontiguousarray(scores, dtype=np.float32)).to(d)
     rl = None if row_lens is None else torch.from_numpy(np.asarray(row_lens, np.int32)).to(d)
     out = torch.full((scores.shape[0], k), 12345, dtype=torch.int32, device=d)
-    mv.select_topk(s, k, out, row_lens=rl, row_len=row_len)
+    mv.select_topk(s, k, out, row_lens=rl, row_len=row_len, split_rows=split_rows)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -38,15 +38,23 @@ CASES = [
     ("k_over_n", lambda r: r.standard_normal((2, 300)), 512, None),
     ("ragged_rows", lambda r: r.standard_normal((5, 4096)), 700, [4096, 0, 1, 699, 2500]),
     ("one_bin", lambda r: 1.0 + r.integers(0, 3, size=(2, 5000)) * 2.0 ** -20, 1234, None),
+    # rows long enough to be cut into several pieces (several workgroups per row)
+    ("ties_long", lambda r: r.integers(-3, 4, size=(3, 40000)), 5000, None),
+    ("all_equal_long", lambda r: np.full((2, 20000), -1.5), 7777, None),
+    ("ragged_long", lambda r: r.standard_normal((4, 50000)), 3000, [50000, 8191, 4097, 0]),
+    ("k_over_n_long", lambda r: r.standard_normal((2, 9000)), 12000, None),
+    ("low_bits_long", lambda r: 1.0 + r.integers(0, 5, size=(2, 30000)) * 2.0 ** -22, 10001, None),
 ]
 
 
+@pytest.mark.parametrize("split_rows", [True, False], ids=["pieces", "one_wg"])
 @pytest.mark.parametrize("name,make,k,row_lens", CASES, ids=[c[0] for c in CASES])
-def test_topk_matches_oracle(gpu_lib, name, make, k, row_lens):
+def test_topk_matches_oracle(gpu_lib, name, make, k, row_lens, split_rows):
     rng = np.random.default_rng(abs(k) + 7)
     scores = make(rng).astype(np.float32)
-    print(f"[case] topk {name} rows={scores.shape[0]} L={scores.shape[1]} k={k}", flush=True)
-    got = _run(scores, k, row_lens)
+    print(f"[case] topk {name} rows={scores.shape[0]} L={scores.shape[1]} k={k} "
+          f"split_rows={split_rows}", flush=True)
+    got = _run(scores, k, row_lens, split_rows=split_rows)
     assert np.array_equal(got, _expect(scores, k, row_lens))
 
 
@@ -61,6 +69,11 @@ def test_topk_special_values_and_stride(gpu_lib):
     print("[case] topk special values, row_len 1000 of stride 1100", flush=True)
     got = _run(scores, 400, row_len=1000)
     assert np.array_equal(got, _expect(scores, 400, row_len=1000))
+    # the same values over rows long enough to be cut into pieces
+    big = np.tile(scores, (1, 12))
+    print("[case] topk special values, row_len 12000 of stride 13200", flush=True)
+    got = _run(big, 3000, row_len=12000)
+    assert np.array_equal(got, _expect(big, 3000, row_len=12000))
 
 
 def test_topk_long_rows(gpu_lib):
@@ -70,8 +83,10 @@ def test_topk_long_rows(gpu_lib):
     lens = np.full(32, 131072, np.int32)
     lens[3] = 70000
     print("[case] topk 32 x 131072, k=2048", flush=True)
-    got = _run(scores, 2048, lens)
-    assert np.array_equal(got, _expect(scores, 2048, lens))
+    exp = _expect(scores, 2048, lens)
+    for split_rows in (True, False):
+        got = _run(scores, 2048, lens, split_rows=split_rows)
+        assert np.array_equal(got, exp), f"split_rows={split_rows}"
 
 
 def test_topk_feeds_sparse_attention(gpu_lib):
