@@ -817,74 +817,52 @@ mla_split_kernel(MainArgs a) {
 // ---------------------------------------------------------------------------
 static_assert(16 * 256 * 4 == kRecElems, "16 combine blocks of 256 threads x 4 dims cover one wave record");
 
-template <int MODE>
-__global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
-  constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
-  __shared__ float wts[kRowsPerWave][kMaxSplits + 1];  // unnormalised weight x fp16 scale
-  __shared__ float red[3][8][kRowsPerWave];
-  __shared__ float row_lse[kRowsPerWave];
-  __shared__ float row_inv[kRowsPerWave];  // 1 / sum of the unnormalised weights
-
-  const int bid = blockIdx.x;
-  const int db = bid & 15;
-  const int wrec = bid >> 4;
-  const int wave = wrec & 3;
-  const int rbg = wrec >> 2;
-  const int rb = rbg % a.row_blocks;
-  const int group = rbg / a.row_blocks;
+// The combine of one block once its split count is known; KBATCH (8, 16, 32) is
+// the number of splits whose loads are issued together, chosen from the count
+// so that a block with few splits issues no loads it does not use.
+template <int KBATCH>
+__device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMaxSplits + 1],
+                                             float (*red)[8][kRowsPerWave], float* row_lse,
+                                             float* row_inv, int rb, int group, int wave, int db,
+                                             int n_active, int64_t rec0, int64_t rec_stride) {
+  constexpr int kBatch = KBATCH;
   const int t = threadIdx.x;
-  if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;  // padding wave record
-
-  const GroupInfo gi = group_info(a, group, kSparseMode);
-  int n_active;
-  int64_t rec0, rec_stride;  // record of split 0 of this (group, rb, wave); step per split
-  if (kSparseMode) {
-    n_active = min(a.num_splits, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
-    rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
-    rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
-  } else {
-    int slot0;
-    if (a.num_groups == 1) {
-      slot0 = 0;
-      n_active = min(a.split_slots, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
-    } else {
-      const int2 m = a.ws_meta[group];  // written by the split kernel
-      slot0 = m.x;
-      n_active = m.y;
-    }
-    rec0 = ((int64_t)slot0 * a.row_blocks + rb) * kWaves + wave;
-    rec_stride = (int64_t)a.row_blocks * kWaves;
-  }
-  if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
   const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
 
-  // The first kBatch splits' partials (4 dims of one row per thread) are
-  // loaded before the weights are formed, so the two memory round trips overlap
-  // (and with at most kBatch splits there is no other).
-  constexpr int kBatch = 32;
+  // Loads are issued statistics first, then the first kBatch splits' partials
+  // (4 dims of one row per thread): loads complete in issue order, so the
+  // weights are formed while the partials stream in (with at most kBatch
+  // splits there is no other round trip).
   const int lane = t & 63, qq = t >> 6, half = lane >> 5, l32 = lane & 31;
+  const int r = t & 31, sl = t >> 5;  // phase 1: 8 split lanes per row
+  const float* st = a.ws_lse + rec0 * (kRecRowStats * kRowsPerWave) + r;
+  // The first kBatch splits' statistics stay in registers (one load each).
+  // Every load is issued unconditionally (past the last split it re-reads that
+  // split, and the value is not used): straight-line loads let the compiler
+  // wait for the statistics alone before phase 1 while the partials are still
+  // in flight, where branches around each load made it wait for nearly all.
+  constexpr int kHeld = kBatch / 8;
+  float h_le[kHeld], h_lq[kHeld], h_sc[kHeld];
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i) {
+    const int s = sl + 8 * i;
+    const int sc = min(s, n_active - 1);
+    const float le = st[sc * st_step], lq = st[sc * st_step + kRowsPerWave];
+    const float sf = st[sc * st_step + 2 * kRowsPerWave];
+    const bool v = s < n_active;
+    h_le[i] = v ? le : -__builtin_inff();
+    h_lq[i] = v ? lq : -__builtin_inff();
+    h_sc[i] = v ? sf : 0.f;
+  }
   const uint16_t* o_p = a.ws_o + rec0 * kRecElems + ((db * 4 + qq) * 64 + lane) * 4;
   const int64_t o_step = rec_stride * kRecElems;
   uint2 raw[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    raw[j] = j < n_active ? *reinterpret_cast<const uint2*>(o_p + j * o_step) : uint2{0u, 0u};
+    raw[j] = *reinterpret_cast<const uint2*>(o_p + min(j, n_active - 1) * o_step);
 
   // ---- phase 1: per-row maxima, sums and weights (thread = row x split lane) ----
   {
-    const int r = t & 31, sl = t >> 5;  // 8 split lanes per row
-    const float* st = a.ws_lse + rec0 * (kRecRowStats * kRowsPerWave) + r;
-    // the statistics of the first kBatch splits stay in registers (one load each)
-    constexpr int kHeld = kBatch / 8;
-    float h_le[kHeld], h_lq[kHeld], h_sc[kHeld];
-#pragma unroll
-    for (int i = 0; i < kHeld; ++i) {
-      const int s = sl + 8 * i;
-      const bool v = s < n_active;
-      h_le[i] = v ? st[s * st_step] : -__builtin_inff();
-      h_lq[i] = v ? st[s * st_step + kRowsPerWave] : -__builtin_inff();
-      h_sc[i] = v ? st[s * st_step + 2 * kRowsPerWave] : 0.f;
-    }
     float mx = -__builtin_inff(), mxq = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < kHeld; ++i) {
@@ -971,6 +949,53 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   pkd.y = pack_bf16x2(acc[2], acc[3]);
   *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
   if (db == 0 && qq == 0 && half == 0) a.lse[qrow] = row_lse[l32];
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
+  constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
+  __shared__ float wts[kRowsPerWave][kMaxSplits + 1];  // unnormalised weight x fp16 scale
+  __shared__ float red[3][8][kRowsPerWave];
+  __shared__ float row_lse[kRowsPerWave];
+  __shared__ float row_inv[kRowsPerWave];  // 1 / sum of the unnormalised weights
+
+  const int bid = blockIdx.x;
+  const int db = bid & 15;
+  const int wrec = bid >> 4;
+  const int wave = wrec & 3;
+  const int rbg = wrec >> 2;
+  const int rb = rbg % a.row_blocks;
+  const int group = rbg / a.row_blocks;
+  const int t = threadIdx.x;
+  if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;  // padding wave record
+
+  const GroupInfo gi = group_info(a, group, kSparseMode);
+  int n_active;
+  int64_t rec0, rec_stride;  // record of split 0 of this (group, rb, wave); step per split
+  if (kSparseMode) {
+    n_active = min(a.num_splits, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
+    rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
+    rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
+  } else {
+    int slot0;
+    if (a.num_groups == 1) {
+      slot0 = 0;
+      n_active = min(a.split_slots, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
+    } else {
+      const int2 m = a.ws_meta[group];  // written by the split kernel
+      slot0 = m.x;
+      n_active = m.y;
+    }
+    rec0 = ((int64_t)slot0 * a.row_blocks + rb) * kWaves + wave;
+    rec_stride = (int64_t)a.row_blocks * kWaves;
+  }
+  if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
+  if (n_active <= 8)
+    combine_rows<8>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_active, rec0, rec_stride);
+  else if (n_active <= 16)
+    combine_rows<16>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_active, rec0, rec_stride);
+  else
+    combine_rows<32>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_active, rec0, rec_stride);
 }
 
 // ---------------------------------------------------------------------------

@@ -92,3 +92,41 @@ def test_streams_equal_eager(gpu_lib):
         torch.cuda.synchronize()
         for k in range(n):
             assert torch.equal(outs[k], refs[k][0]) and torch.equal(lses[k], refs[k][1]), (rep, k)
+
+
+def test_topk_graph_replay_equals_eager(gpu_lib):
+    """Top-k over row pieces (five launches sharing a workspace) captured into a
+    graph: every replay, with the workspace and output scribbled over and other
+    eager selections in between, equals the eager call."""
+    import speculative_decode_verify_mla_amd as mv
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(71)
+    R, L, k = 6, 30000, 1500
+    scores = torch.from_numpy(rng.standard_normal((R, L)).astype(np.float32)).to(dev)
+    lens = torch.tensor([30000, 12000, 4097, 0, 29999, 1], dtype=torch.int32, device=dev)
+    ws = torch.empty(mv.topk_workspace_bytes(R, L), dtype=torch.uint8, device=dev)
+    out = torch.empty((R, k), dtype=torch.int32, device=dev)
+    print(f"[case] top-k graph replay R={R} L={L} k={k} workspace={ws.numel()}", flush=True)
+    mv.select_topk(scores, k, out, row_lens=lens, workspace=ws)
+    torch.cuda.synchronize()
+    ref = out.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    mv.select_topk(scores, k, out, row_lens=lens, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        mv.select_topk(scores, k, out, row_lens=lens, workspace=ws, stream=side)
+    torch.cuda.synchronize()
+    other = torch.flip(scores, dims=[1]).contiguous()
+    other_out = torch.empty_like(out)
+    for rep in range(3):
+        out.fill_(-7)
+        ws.fill_(0xAB)
+        mv.select_topk(other, k, other_out, row_lens=lens, workspace=ws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}"
