@@ -7,6 +7,12 @@
 // by lower position, which makes the selected set unique; the result is
 // written in ascending position order, -1 padded to k.
 //
+// Two paths with identical results. Called without a workspace, one workgroup
+// of 1024 threads per row (mla_topk_kernel, below). With one, a batch of rows
+// too short to fill the GPU is spread over several workgroups per row
+// (mla_topk_level_kernel x 4, mla_topk_place_kernel; see the section further
+// down).
+//
 // One workgroup of 1024 threads per row:
 //  * Radix select of the k-th key over an order-preserving 32-bit map of the
 //    scores, in three passes of 12, 12 and 8 bits: each pass histograms the
