@@ -330,8 +330,12 @@ int mla_head_project(int32_t tokens, int32_t heads, int32_t in_dim, int32_t out_
 
 size_t mla_select_topk_workspace_bytes(int32_t rows, int32_t row_len) {
   if (rows < 1 || row_len < 1) return 0;
+  // Any device cuts a row into at most `pieces` pieces (the count for unlimited
+  // CUs) of whole 1024-score steps, so pieces x chunk <= row_len + 1024 x pieces.
   const int pieces = topk_pieces(rows, row_len, INT32_MAX / 4, nullptr);
-  return pieces > 1 ? (size_t)mlav::topk_workspace_bytes(rows, pieces) : 0;
+  if (pieces <= 1) return 0;
+  return (size_t)((int64_t)rows * pieces * mlav::topk_piece_bytes +
+                  (int64_t)rows * ((int64_t)row_len + 1024 * (int64_t)pieces) * 8);
 }
 
 int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k,
@@ -344,7 +348,7 @@ int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k
     return MLA_ERR_INVALID;
   int chunk = row_len;
   const int pieces = workspace ? topk_pieces(rows, row_len, device_cus(), &chunk) : 1;
-  if (pieces > 1 && workspace_bytes < (size_t)mlav::topk_workspace_bytes(rows, pieces))
+  if (pieces > 1 && workspace_bytes < (size_t)mlav::topk_workspace_bytes(rows, pieces, chunk))
     return MLA_ERR_WORKSPACE;
   const int rc = check_device();
   if (rc != MLA_OK) return rc;

@@ -107,10 +107,12 @@ struct TopkArgs {
 constexpr int kTopkMaxChunks = 32;   // pieces per row
 constexpr int kTopkMinChunk = 4096;  // scores per piece, at least
 constexpr int kTopkLevels = 4;       // 8-bit digits of the 32-bit order key
-// Workspace bytes of the several-workgroup path for `rows` rows and `chunks` pieces.
-constexpr int64_t topk_workspace_bytes(int64_t rows, int64_t chunks) {
-  return (int64_t)kTopkLevels * rows * chunks * 256 * 4 + rows * kTopkLevels * 16 +
-         (int64_t)(kTopkLevels - 1) * rows * chunks * 4;
+// Workspace bytes of the several-workgroup path for `rows` rows cut into
+// `chunks` pieces of `chunk` scores: per piece a 256-bin histogram and two
+// counts per wave segment, and candidate room for every score (8 bytes each).
+constexpr int64_t topk_piece_bytes = 256 * 4 + 16 + 16;
+constexpr int64_t topk_workspace_bytes(int64_t rows, int64_t chunks, int64_t chunk) {
+  return rows * chunks * topk_piece_bytes + rows * chunks * chunk * 8;
 }
 hipError_t launch_topk_kernel(const TopkArgs& a, hipStream_t stream);
 

@@ -10,8 +10,8 @@
 // Two paths with identical results. Called without a workspace, one workgroup
 // of 1024 threads per row (mla_topk_kernel, below). With one, a batch of rows
 // too short to fill the GPU is spread over several workgroups per row
-// (mla_topk_level_kernel x 4, mla_topk_place_kernel; see the section further
-// down).
+// (mla_topk_hist_kernel, mla_topk_compact_kernel, mla_topk_place_kernel; see
+// the section further down).
 //
 // One workgroup of 1024 threads per row:
 //  * Radix select of the k-th key over an order-preserving 32-bit map of the
@@ -52,16 +52,24 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts within each
+// 16-lane row, then the row broadcasts (lane 15 into rows 1 and 3, lane 31
+// into rows 2 and 3). Lane-to-lane data paths, no LDS round trips.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Block-wide exclusive prefix of one count per thread; `total` gets the sum.
 // Every thread of the block must call it (it synchronises twice).
 __device__ int block_excl_scan(int v, int* wave_tot, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) wave_tot[wave] = x;
   __syncthreads();
   int below = 0, tot = 0;
@@ -218,13 +226,8 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_kernel(TopkArgs a) {
       }
       // wave-exclusive prefix of (cg, ce), packed as cg | ce << 16
       const int packed = cg | (ce << 16);
-      int incl = packed;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      const int step_tot = __shfl(incl, 63);
+      const int incl = wave_incl_scan(packed);
+      const int step_tot = __builtin_amdgcn_readlane(incl, 63);
       int g = G + ((incl - packed) & 0xffff), eqb = E + ((incl - packed) >> 16);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -245,56 +248,57 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_kernel(TopkArgs a) {
 // ---------------------------------------------------------------------------
 // Several workgroups per row. With few rows, one workgroup per row leaves most
 // CUs idle, so each row is cut into `chunks` pieces, one 256-thread workgroup
-// per (row, piece), and the radix select runs over 8-bit digits in four
-// launches, most significant digit first. Launch L:
-//  * every workgroup of a row first settles digit L-1: it sums the pieces'
-//    level L-1 histograms (256 bins x pieces) and finds the bin where the count
-//    of larger keys reaches the number still to take (all workgroups of the
-//    row reach the same answer; piece 0 records the new state for launch L+1)
-//    and records its own count of keys in the bins above the settled digit;
-//  * then it histograms digit L of its piece's keys that match the digits
-//    fixed so far and stores the 256 counts (no atomics outside LDS, no
-//    clearing: every piece writes all of its bins).
-// A fifth launch settles the last digit, which gives the threshold key T and
-// how many keys equal to T are taken. A piece's count of keys above T is the
-// sum over levels of its keys above that level's digit, and its count of keys
-// equal to T is its last-level bin of T, so the pieces before it give each
-// piece its output offsets. The piece then places its selected positions in
-// position order as the one-workgroup kernel does.
+// per (row, piece), in three launches:
+//  1. mla_topk_hist_kernel: each piece histograms the top 8 bits (digit 0) of
+//     its keys and stores the 256 counts.
+//  2. mla_topk_compact_kernel: every workgroup of a row sums the pieces'
+//     histograms and finds the digit-0 bin d0 where the count of larger keys
+//     reaches k (all reach the same answer). Keys above d0 are all selected;
+//     keys in bin d0 are candidates. Each wave walks its segment of the piece,
+//     records how many keys it has above d0, and writes its candidates
+//     (position, key), in position order, to a region of its own.
+//  3. mla_topk_place_kernel: every workgroup of a row gathers the row's
+//     candidates (usually a few percent of the row) into LDS and settles the
+//     remaining three 8-bit digits over them, which gives the threshold key T
+//     and how many keys equal to T are taken. Each (piece, wave) segment's
+//     count of keys above T is its count above d0 plus its candidates above T,
+//     its count equal to T is its candidates equal to T, so a prefix over the
+//     segments gives every wave its output offsets, and each wave places its
+//     segment's selected positions in one walk, in position order.
+// The workspace holds the histograms, the counts and the candidate regions
+// (room for every key of a row: a row whose keys share their top 8 bits is
+// correct, only slower). Every call rewrites what it reads.
 // ---------------------------------------------------------------------------
 constexpr int kMwThreads = 256;
 constexpr int kMwWaves = kMwThreads / 64;
+constexpr int kMwRegions = 4 * kTopkMaxChunks;  // (piece, wave) candidate regions per row, at most
+static_assert(kMwRegions <= kMwThreads, "one region count per thread");
+constexpr int kCandLds = 8192;  // candidate keys of a row staged in LDS (more: read from L2)
 
-struct MwState {
-  uint32_t prefix, pmask;  // digits fixed so far, and their bits
-  int32_t k_rem, pad;      // keys still to take among those matching prefix
+struct MwLayout {
+  uint32_t* hist;   // [rows][chunks][256] digit-0 counts
+  int* above;       // [rows][chunks][4] keys above d0 per (piece, wave) segment
+  int* ccount;      // [rows][chunks][4] candidates per (piece, wave)
+  uint2* cand;      // [rows][chunks][4][chunk / 4] (position, key)
 };
-
-__device__ __forceinline__ uint32_t* mw_hist(const TopkArgs& a, int level, int row, int piece) {
-  return reinterpret_cast<uint32_t*>(a.ws) +
-         (((int64_t)level * a.rows + row) * a.chunks + piece) * 256;
-}
-__device__ __forceinline__ MwState* mw_state(const TopkArgs& a, int row, int level) {
-  uint8_t* base = reinterpret_cast<uint8_t*>(a.ws) + (int64_t)kTopkLevels * a.rows * a.chunks * 256 * 4;
-  return reinterpret_cast<MwState*>(base) + (int64_t)row * kTopkLevels + level;
-}
-// Keys of a piece whose digit `level` (< kTopkLevels - 1) is above the settled
-// one (they match the digits above it): written by launch level + 1.
-__device__ __forceinline__ int* mw_above(const TopkArgs& a, int level, int row, int piece) {
-  uint8_t* base = reinterpret_cast<uint8_t*>(a.ws) + (int64_t)kTopkLevels * a.rows * a.chunks * 256 * 4 +
-                  (int64_t)a.rows * kTopkLevels * 16;
-  return reinterpret_cast<int*>(base) + ((int64_t)level * a.rows + row) * a.chunks + piece;
+__device__ __forceinline__ MwLayout mw_layout(const TopkArgs& a) {
+  uint8_t* p = reinterpret_cast<uint8_t*>(a.ws);
+  const int64_t rp = (int64_t)a.rows * a.chunks;
+  MwLayout l;
+  l.hist = reinterpret_cast<uint32_t*>(p);
+  p += rp * 256 * 4;
+  l.above = reinterpret_cast<int*>(p);
+  p += rp * 4 * 4;
+  l.ccount = reinterpret_cast<int*>(p);
+  p += rp * 4 * 4;
+  l.cand = reinterpret_cast<uint2*>(p);
+  return l;
 }
 
 // Block-wide exclusive prefix over the 256 threads (one count each).
 __device__ int mw_excl_scan(int v, int* wave_tot, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) wave_tot[wave] = x;
   __syncthreads();
   int below = 0, tot = 0;
@@ -309,30 +313,38 @@ __device__ int mw_excl_scan(int v, int* wave_tot, int& total) {
   return below + x - v;
 }
 
-// Settles digit `level` of a row from the pieces' level histograms: returns
-// the digit; `taken_above` gets the count of matching keys in higher bins.
-// Every thread of the block must call it; requires k_rem >= 1.
-__device__ uint32_t mw_settle(const TopkArgs& a, int row, int level, int k_rem, int* wave_tot,
-                              uint32_t* s_digit, int* s_above, int& taken_above) {
-  const int tid = threadIdx.x;
-  uint32_t v[kTopkMaxChunks];  // every piece's count of this bin, all loads in flight
-#pragma unroll
-  for (int i = 0; i < kTopkMaxChunks; ++i) v[i] = i < a.chunks ? mw_hist(a, level, row, i)[tid] : 0u;
-  int c = 0;
-#pragma unroll
-  for (int i = 0; i < kTopkMaxChunks; ++i) c += (int)v[i];
+// Thread t holds the count c of bin t of a 256-bin histogram of the keys that
+// match the digits fixed so far. Returns the bin where the count of keys in
+// higher bins first reaches k_rem (>= 1, and at most the total); `above` gets
+// that count. Every thread of the block must call it.
+__device__ uint32_t mw_pick(int c, int k_rem, int* wave_tot, uint32_t* s_digit, int* s_above,
+                            int& above) {
   int total;
   const int excl = mw_excl_scan(c, wave_tot, total);
-  const int above = total - excl - c;  // matching keys in bins above this thread's
-  if (above < k_rem && k_rem <= above + c) {  // exactly one bin of the block
-    *s_digit = (uint32_t)tid;
-    *s_above = above;
+  const int hi = total - excl - c;  // keys in bins above this thread's
+  if (hi < k_rem && k_rem <= hi + c) {  // exactly one bin of the block
+    *s_digit = (uint32_t)threadIdx.x;
+    *s_above = hi;
   }
   __syncthreads();
   const uint32_t d = *s_digit;
-  taken_above = *s_above;
+  above = *s_above;
   __syncthreads();
   return d;
+}
+
+// The digit-0 bin of a row from its pieces' histograms (all loads in flight).
+__device__ uint32_t mw_settle0(const TopkArgs& a, const MwLayout& l, int row, int kk, int* wave_tot,
+                               uint32_t* s_digit, int* s_above, int& above) {
+  const int tid = threadIdx.x;
+  uint32_t v[kTopkMaxChunks];  // unconditional loads (clamped), masked in the sum
+#pragma unroll
+  for (int i = 0; i < kTopkMaxChunks; ++i)
+    v[i] = l.hist[((int64_t)row * a.chunks + min(i, a.chunks - 1)) * 256 + tid];
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkMaxChunks; ++i) c += i < a.chunks ? (int)v[i] : 0;
+  return mw_pick(c, kk, wave_tot, s_digit, s_above, above);
 }
 
 __device__ __forceinline__ int mw_row_len(const TopkArgs& a, int row) {
@@ -340,85 +352,124 @@ __device__ __forceinline__ int mw_row_len(const TopkArgs& a, int row) {
   return n < 0 ? 0 : (n > a.row_len ? a.row_len : n);
 }
 
-// Histogram copies in LDS for the first digit: lanes add to copy lane % 16 (at
-// most 4 lanes of a wave instruction per address when keys share a bin, as the
-// top digits of real scores do), 257-word stride so one bin's copies sit in 16
-// different banks. Later digits only count the few keys matching the digits
-// fixed so far and use one copy.
+// Histogram copies in LDS for digit 0: lanes add to copy lane % 16 (at most 4
+// lanes of a wave instruction per address when keys share a bin, as the top
+// digits of real scores do), 257-word stride so one bin's copies sit in 16
+// different banks.
 constexpr int kHistCopies = 16;
 constexpr int kHistStride = 257;
 
-__global__ void __launch_bounds__(kMwThreads) mla_topk_level_kernel(TopkArgs a, int level) {
+__global__ void __launch_bounds__(kMwThreads) mla_topk_hist_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kHistCopies * kHistStride];
-  __shared__ int wave_tot[kMwWaves];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_above;
   const int row = blockIdx.x / a.chunks, piece = blockIdx.x - row * a.chunks;
   const int tid = threadIdx.x;
   const int n = mw_row_len(a, row);
-  const int kk = min(a.k, n);
-
-  MwState st{0u, 0u, kk, 0};
-  if (level > 0) {
-    st = *mw_state(a, row, level - 1);
-    if (kk > 0) {
-      const int shift = 24 - 8 * (level - 1);
-      int taken;
-      const uint32_t d = mw_settle(a, row, level - 1, st.k_rem, wave_tot, &s_digit, &s_above, taken);
-      st.prefix |= d << shift;
-      st.pmask |= 0xffu << shift;
-      st.k_rem -= taken;
-      // this piece's keys above the settled digit (block sum over the bins above d)
-      const int mine = (uint32_t)tid > d ? (int)mw_hist(a, level - 1, row, piece)[tid] : 0;
-      int piece_above;
-      mw_excl_scan(mine, wave_tot, piece_above);
-      if (tid == 0) *mw_above(a, level - 1, row, piece) = piece_above;
-    } else if (tid == 0) {
-      *mw_above(a, level - 1, row, piece) = 0;
-    }
-  }
-  if (piece == 0 && tid == 0) *mw_state(a, row, level) = st;
-
-  const int copies = level == 0 ? kHistCopies : 1;
-  for (int i = tid; i < copies * kHistStride; i += kMwThreads) hist[i] = 0u;
+  for (int i = tid; i < kHistCopies * kHistStride; i += kMwThreads) hist[i] = 0u;
   __syncthreads();
-  const int shift = 24 - 8 * level;
-  uint32_t* const my_hist = hist + (tid & (copies - 1)) * kHistStride;
+  uint32_t* const my_hist = hist + (tid & (kHistCopies - 1)) * kHistStride;
   const int p0 = piece * a.chunk, p1 = min(p0 + a.chunk, n);
   const float* s = a.scores + (int64_t)row * a.row_stride;
   constexpr int kSpan = 4 * kMwThreads;
   constexpr int kBatch = 8;  // 8 x 16 bytes per thread in flight
-  if (kk > 0) {
-    for (int base = p0; base < p1; base += kBatch * kSpan) {
-      float4 v[kBatch];
+  for (int base = p0; base < p1; base += kBatch * kSpan) {
+    float4 v[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int p = base + j * kSpan + 4 * tid;
-        v[j] = p < p1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = base + j * kSpan + 4 * tid;
+      v[j] = p < p1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int p = base + j * kSpan + 4 * tid;
-        const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = base + j * kSpan + 4 * tid;
+      const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t u = order_key(e[q]);
-          if (p + q < p1 && (u & st.pmask) == st.prefix) atomicAdd(&my_hist[(u >> shift) & 0xffu], 1u);
-        }
-      }
+      for (int q = 0; q < 4; ++q)
+        if (p + q < p1) atomicAdd(&my_hist[order_key(e[q]) >> 24], 1u);
     }
   }
   __syncthreads();
   uint32_t c = 0u;
-  for (int i = 0; i < copies; ++i) c += hist[i * kHistStride + tid];
-  mw_hist(a, level, row, piece)[tid] = c;
+#pragma unroll
+  for (int i = 0; i < kHistCopies; ++i) c += hist[i * kHistStride + tid];
+  const MwLayout l = mw_layout(a);
+  l.hist[((int64_t)row * a.chunks + piece) * 256 + tid] = c;
 }
 
-__global__ void __launch_bounds__(kMwThreads) mla_topk_place_kernel(TopkArgs a) {
+__global__ void __launch_bounds__(kMwThreads) mla_topk_compact_kernel(TopkArgs a) {
   __shared__ int wave_tot[kMwWaves];
   __shared__ uint32_t s_digit;
   __shared__ int s_above;
+  const int row = blockIdx.x / a.chunks, piece = blockIdx.x - row * a.chunks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = mw_row_len(a, row);
+  const int kk = min(a.k, n);
+  const MwLayout l = mw_layout(a);
+  const int64_t rp = (int64_t)row * a.chunks + piece;
+  const int seg = a.chunk / kMwWaves;  // whole 256-score steps (chunk is a multiple of 1024)
+  uint2* const region = l.cand + (rp * kMwWaves + wave) * seg;
+  if (kk == 0) {  // nothing selected: empty candidate regions
+    if (lane == 0) {
+      l.ccount[rp * kMwWaves + wave] = 0;
+      l.above[rp * kMwWaves + wave] = 0;
+    }
+    return;
+  }
+  int taken;
+  const uint32_t d0 = mw_settle0(a, l, row, kk, wave_tot, &s_digit, &s_above, taken);
+
+  // this wave's segment: count the keys above bin d0 (all selected) and write
+  // the candidates (keys in bin d0) in position order
+  const float* s = a.scores + (int64_t)row * a.row_stride;
+  const int p1 = min(piece * a.chunk + a.chunk, n);
+  const int w0 = piece * a.chunk + wave * seg, w1 = min(w0 + seg, p1);
+  int count = 0, n_above = 0;
+  for (int base = w0; base < w1; base += kWalkBatch * 256) {
+    float4 vb[kWalkBatch];
+#pragma unroll
+    for (int j = 0; j < kWalkBatch; ++j) {
+      const int p = base + 256 * j + 4 * lane;
+      vb[j] = p < w1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < kWalkBatch; ++j) {
+      const int p = base + 256 * j + 4 * lane;
+      const float e[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+      uint32_t u[4];
+      bool c[4];
+      int cn = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u[q] = order_key(e[q]);
+        c[q] = p + q < w1 && (u[q] >> 24) == d0;
+        cn += c[q];
+        n_above += (p + q < w1 && (u[q] >> 24) > d0);
+      }
+      const int incl = wave_incl_scan(cn);
+      int at = count + incl - cn;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (c[q]) region[at++] = make_uint2((uint32_t)(p + q), u[q]);
+      }
+      count += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  n_above = wave_sum_i(n_above);
+  if (lane == 0) {
+    l.ccount[rp * kMwWaves + wave] = count;
+    l.above[rp * kMwWaves + wave] = n_above;
+  }
+}
+
+__global__ void __launch_bounds__(kMwThreads) mla_topk_place_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ int wave_tot[kMwWaves];
+  __shared__ uint32_t s_digit;
+  __shared__ int s_above;
+  __shared__ int cnt[kMwRegions];
+  __shared__ int off[kMwRegions + 1];  // exclusive prefix of cnt over the regions
+  __shared__ uint32_t ck[kCandLds];    // the row's candidate keys, in position order
   __shared__ int seg_gt[kMwWaves], seg_eq[kMwWaves];
+  __shared__ int rg_gt[kMwRegions], rg_eq[kMwRegions];  // per region: keys above / equal to T
   const int row = blockIdx.x / a.chunks, piece = blockIdx.x - row * a.chunks;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = mw_row_len(a, row);
@@ -426,74 +477,143 @@ __global__ void __launch_bounds__(kMwThreads) mla_topk_place_kernel(TopkArgs a) 
   int32_t* out = a.indices + (int64_t)row * a.k;
 
   if (kk > 0) {
-    MwState st = *mw_state(a, row, kTopkLevels - 1);
+    const MwLayout l = mw_layout(a);
+    const int regions = a.chunks * kMwWaves;
+    const int seg = a.chunk / kMwWaves;
+    const uint2* const rc = l.cand + (int64_t)row * regions * seg;
+    // Every load the prologue needs is issued at once, unconditionally (indices
+    // clamped into range, unused values masked afterwards), so one memory round
+    // trip covers the digit-0 histograms, the region counts and the first 64
+    // candidates of every region. Wave w takes region 4j + w in slot j.
+    constexpr int kSlots = kMwRegions / kMwWaves;
+    uint32_t hv[kTopkMaxChunks];
+#pragma unroll
+    for (int i = 0; i < kTopkMaxChunks; ++i)
+      hv[i] = l.hist[((int64_t)row * a.chunks + min(i, a.chunks - 1)) * 256 + tid];
+    const int rt = min(tid, regions - 1);
+    const int c_ld = l.ccount[(int64_t)row * regions + rt];
+    const int ab_ld = l.above[(int64_t)row * regions + rt];
+    uint32_t v[kSlots];
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) v[j] = rc[(int64_t)min(4 * j + wave, regions - 1) * seg + lane].y;
+
+    int c0 = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkMaxChunks; ++i) c0 += i < a.chunks ? (int)hv[i] : 0;
     int taken;
-    const uint32_t d = mw_settle(a, row, kTopkLevels - 1, st.k_rem, wave_tot, &s_digit, &s_above, taken);
-    const uint32_t T = st.prefix | d;  // the threshold key
-    const int k_eq = st.k_rem - taken;  // keys equal to T that are taken
-
-    // keys above / equal to T in the pieces before this one
-    // Earlier levels: the recorded per-piece counts (thread i < pieces, level
-    // i / pieces); last level: bin counts of the pieces before this one.
-    int g_part = 0, e_part = 0;
-    for (int t = tid; t < (kTopkLevels - 1) * a.chunks; t += kMwThreads) {
-      const int lv = t / a.chunks, i = t - lv * a.chunks;
-      if (i < piece) g_part += *mw_above(a, lv, row, i);
-    }
-    {
-      const bool above = (uint32_t)tid > d, at = (uint32_t)tid == d;
-      uint32_t v[kTopkMaxChunks];  // pieces before this one, all loads in flight
-#pragma unroll
-      for (int i = 0; i < kTopkMaxChunks; ++i)
-        v[i] = (i < piece && (above || at)) ? mw_hist(a, kTopkLevels - 1, row, i)[tid] : 0u;
-#pragma unroll
-      for (int i = 0; i < kTopkMaxChunks; ++i) {
-        g_part += above ? (int)v[i] : 0;
-        e_part += at ? (int)v[i] : 0;
+    const uint32_t d0 = mw_pick(c0, kk, wave_tot, &s_digit, &s_above, taken);
+    int k_rem = kk - taken;  // keys still to take among the candidates (bin d0)
+    {  // region counts and their exclusive prefix (at most 128 regions: one per thread)
+      const int c = tid < regions ? c_ld : 0;
+      int total;
+      const int ex = mw_excl_scan(c, wave_tot, total);
+      if (tid < regions) {
+        cnt[tid] = c;
+        off[tid] = ex;
+        rg_gt[tid] = ab_ld;  // keys above bin d0; candidates above T are added below
+        rg_eq[tid] = 0;
       }
+      if (tid == 0) off[regions] = total;
+      __syncthreads();
     }
-    int G0, E0;
-    mw_excl_scan(g_part, wave_tot, G0);
-    mw_excl_scan(e_part, wave_tot, E0);
-
-    // Each wave owns one contiguous segment of the piece (whole 256-score steps):
-    // count, exchange the wave totals, then walk again placing positions.
-    const float* s = a.scores + (int64_t)row * a.row_stride;
-    const int p0 = piece * a.chunk, p1 = min(p0 + a.chunk, n);
-    const int len = max(p1 - p0, 0);
-    const int seg = (len + kMwWaves * 256 - 1) / (kMwWaves * 256) * 256;
-    const int w0 = p0 + wave * seg, w1 = min(w0 + seg, p1);
-    int ngt = 0, neq = 0;
-    for (int base = w0; base < w1; base += kWalkBatch * 256) {
-      float4 v[kWalkBatch];
-#pragma unroll
-      for (int j = 0; j < kWalkBatch; ++j) {
-        const int p = base + 256 * j + 4 * lane;
-        v[j] = p < w1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
+    const int n_cand = off[regions];
+    const bool staged = n_cand <= kCandLds;
+    // Candidate key `i` of the row (regions in piece-major order = position order).
+    auto cand_key = [&](int i) -> uint32_t {
+      int lo = 0, hi = regions - 1;  // the region r with off[r] <= i < off[r + 1]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= i) lo = mid; else hi = mid - 1;
       }
+      return rc[(int64_t)lo * seg + (i - off[lo])].y;
+    };
+    // Gather the keys into LDS (staged; candidates past 64 in a region follow in
+    // a second loop), building the digit-1 histogram on the way.
+    hist[tid] = 0u;
+    __syncthreads();
+    if (staged) {
 #pragma unroll
-      for (int j = 0; j < kWalkBatch; ++j) {
-        const int p = base + 256 * j + 4 * lane;
-        const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t u = order_key(e[q]);
-          ngt += (p + q < w1 && u > T);
-          neq += (p + q < w1 && u == T);
+      for (int j = 0; j < kSlots; ++j) {
+        const int r = 4 * j + wave;
+        if (r < regions && lane < cnt[r]) {
+          ck[off[r] + lane] = v[j];
+          atomicAdd(&hist[(v[j] >> 16) & 0xffu], 1u);
         }
       }
-    }
-    const int wgt = wave_sum_i(ngt), weq = wave_sum_i(neq);
-    if (lane == 0) {
-      seg_gt[wave] = wgt;
-      seg_eq[wave] = weq;
+      for (int r = wave; r < regions; r += kMwWaves)
+        for (int e = 64 + lane; e < cnt[r]; e += 64) {
+          const uint32_t u = rc[(int64_t)r * seg + e].y;
+          ck[off[r] + e] = u;
+          atomicAdd(&hist[(u >> 16) & 0xffu], 1u);
+        }
+    } else {
+      for (int i = tid; i < n_cand; i += kMwThreads) atomicAdd(&hist[(cand_key(i) >> 16) & 0xffu], 1u);
     }
     __syncthreads();
-    int G = G0, E = E0;
-    for (int w = 0; w < wave; ++w) {
-      G += seg_gt[w];
-      E += seg_eq[w];
+    auto key_at = [&](int i) -> uint32_t { return staged ? ck[i] : cand_key(i); };
+
+    // digits 1..3 over the candidates (digit 1's histogram is already built)
+    uint32_t prefix = d0 << 24, pmask = 0xff000000u;
+    for (int lv = 1; lv < kTopkLevels; ++lv) {
+      const int shift = 24 - 8 * lv;
+      if (lv > 1) {
+        hist[tid] = 0u;
+        __syncthreads();
+        for (int i = tid; i < n_cand; i += kMwThreads) {
+          const uint32_t u = key_at(i);
+          if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 0xffu], 1u);
+        }
+        __syncthreads();
+      }
+      int above;
+      const uint32_t d = mw_pick((int)hist[tid], k_rem, wave_tot, &s_digit, &s_above, above);
+      prefix |= d << shift;
+      pmask |= 0xffu << shift;
+      k_rem -= above;
     }
+    const uint32_t T = prefix;  // the threshold key
+    const int k_eq = k_rem;     // keys equal to T that are taken
+
+    // Keys above / equal to T in every (piece, wave) segment before this wave's:
+    // a region's count above T is its keys above bin d0 (recorded by the compact
+    // launch) plus its candidates above T (summed by the wave that owns it in
+    // the slot mapping above); an exclusive prefix over the regions gives each
+    // wave of this piece its starting offsets.
+    {
+      const int last = (piece + 1) * kMwWaves;  // regions up to this piece's
+      for (int j = 0; j < kSlots; ++j) {
+        const int r = 4 * j + wave;
+        if (r >= last) break;  // uniform per wave
+        int g = 0, q = 0;
+        for (int e0 = 0; e0 < cnt[r]; e0 += 64) {
+          const bool in = e0 + lane < cnt[r];
+          const uint32_t u = in ? key_at(off[r] + e0 + lane) : 0u;
+          g += __popcll(__ballot(in && u > T));
+          q += __popcll(__ballot(in && u == T));
+        }
+        if (lane == 0) {
+          rg_gt[r] += g;
+          rg_eq[r] = q;
+        }
+      }
+      __syncthreads();
+      const int gt = tid < last ? rg_gt[tid] : 0, eq = tid < last ? rg_eq[tid] : 0;
+      int tg, te;
+      const int xg = mw_excl_scan(gt, wave_tot, tg);
+      const int xe = mw_excl_scan(eq, wave_tot, te);
+      if (tid >= piece * kMwWaves && tid < last) {
+        seg_gt[tid - piece * kMwWaves] = xg;
+        seg_eq[tid - piece * kMwWaves] = xe;
+      }
+      __syncthreads();
+    }
+
+    // Each wave walks its segment of the piece (whole 256-score steps) once,
+    // placing positions by wave-local prefix sums from its starting offsets.
+    const float* s = a.scores + (int64_t)row * a.row_stride;
+    const int p1 = min(piece * a.chunk + a.chunk, n);
+    const int w0 = piece * a.chunk + wave * seg, w1 = min(w0 + seg, p1);
+    int G = seg_gt[wave], E = seg_eq[wave];
     for (int base = w0; base < w1; base += kWalkBatch * 256) {
       float4 vb[kWalkBatch];
 #pragma unroll
@@ -516,13 +636,8 @@ __global__ void __launch_bounds__(kMwThreads) mla_topk_place_kernel(TopkArgs a) 
           ce += eq[q];
         }
         const int packed = cg | (ce << 16);
-        int incl = packed;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o);
-          if (lane >= o) incl += y;
-        }
-        const int step_tot = __shfl(incl, 63);
+        const int incl = wave_incl_scan(packed);
+        const int step_tot = __builtin_amdgcn_readlane(incl, 63);
         int g = G + ((incl - packed) & 0xffff), eqb = E + ((incl - packed) >> 16);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -549,11 +664,12 @@ hipError_t launch_topk_kernel(const TopkArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const unsigned grid = (unsigned)a.rows * (unsigned)a.chunks;
-  for (int level = 0; level < kTopkLevels; ++level) {
-    hipLaunchKernelGGL(mla_topk_level_kernel, dim3(grid), dim3(kMwThreads), 0, stream, a, level);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  hipLaunchKernelGGL(mla_topk_hist_kernel, dim3(grid), dim3(kMwThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_topk_compact_kernel, dim3(grid), dim3(kMwThreads), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_topk_place_kernel, dim3(grid), dim3(kMwThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -218,9 +218,9 @@ def test_topk_and_projection_invalid_arguments(lib):
 
 def test_topk_workspace_bytes(lib):
     w = lib.mla_select_topk_workspace_bytes
-    # 32 pieces of 4096 scores: 4 levels x 32 rows x 32 pieces x 256 bins x 4 B, the
-    # per-row state (4 x 16 B) and 3 levels of per-piece counts (4 B)
-    assert w(32, 131072) == 4 * 32 * 32 * 1024 + 32 * 4 * 16 + 3 * 32 * 32 * 4
+    # at most 32 pieces: per piece 256 bins + 8 counts (4 B each), and candidate
+    # room for every score plus one 1024-score step per piece (8 B each)
+    assert w(32, 131072) == 32 * 32 * 1056 + 32 * (131072 + 32 * 1024) * 8
     assert w(1, 4096) == 0          # one piece: no workspace
-    assert w(3, 9000) == 4 * 3 * 3 * 1024 + 3 * 4 * 16 + 3 * 3 * 3 * 4
+    assert w(3, 9000) == 3 * 3 * 1056 + 3 * (9000 + 3 * 1024) * 8
     assert w(0, 100) == 0 and w(2, 0) == 0
