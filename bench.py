@@ -568,7 +568,7 @@ def bench_topk(args, dev):
         "algorithmic_bytes": nbytes, "achieved_hbm_GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "mla_topk_level_kernel x4 + mla_topk_place_kernel (whole call)"},
+                     "kernel": "mla_topk_hist_kernel + mla_topk_compact_kernel + mla_topk_place_kernel (whole call)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
