@@ -25,7 +25,7 @@ constexpr int kMaxSplits = 256;  // per query group (combine weights live in LDS
 // Fewest 64-key tiles per split when the library picks the split count: the
 // per-split partial (1 KiB per row, written and read back) and the split's fixed
 // start-up stay small next to its KV reads and matrix work.
-constexpr int kMinChunkDense = 4;
+constexpr int kMinChunkDense = 2;
 constexpr int kMinChunkSparse = 4;
 constexpr size_t kRecBytes = (size_t)kRecElems * 2 + (size_t)kRecRowStats * kRowsPerWave * 4;
 
