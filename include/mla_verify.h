@@ -224,8 +224,10 @@ int mla_head_project(int32_t tokens, int32_t heads, int32_t in_dim, int32_t out_
  * workspace: NULL runs one workgroup per row (no scratch memory). With a
  * device buffer of at least mla_select_topk_workspace_bytes(rows, row_len)
  * bytes, rows are spread over several workgroups when there are too few rows
- * to fill the GPU (five kernel launches; the buffer holds per-piece digit
- * histograms and is fully rewritten by every call, so it needs no clearing).
+ * to fill the GPU (three kernel launches; the buffer holds per-piece digit
+ * histograms and counts and room for every score as a candidate, about
+ * 8 bytes per score, and every call writes what it later reads, so it needs no
+ * clearing).
  * A smaller non-NULL buffer than that path needs is MLA_ERR_WORKSPACE. The
  * result is identical either way. Calls sharing one workspace must be ordered
  * on one stream. Enqueued on `stream`. */
@@ -234,7 +236,8 @@ int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes for mla_select_topk's several-workgroup path on any device
- * (0 when rows are never split: row_len <= 4096 or invalid arguments). */
+ * (0 when rows are never split: row_len <= 4096 or invalid arguments):
+ * rows x (up to 32 pieces x 1,056 + (row_len + 1,024 x pieces) x 8). */
 size_t mla_select_topk_workspace_bytes(int32_t rows, int32_t row_len);
 
 /* Static description of an error code (never NULL). */
