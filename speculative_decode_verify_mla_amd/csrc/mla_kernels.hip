@@ -584,20 +584,43 @@ mla_split_kernel(MainArgs a) {
     score_fence(acc);
     return acc;
   };
-  // One slice of the softmax of a half: steps 0..15 exponentiate term `step`
-  // (in place), steps 16..23 pack two terms to bf16 and add them to the rounded sum.
-  auto softmax_step = [&](int step, f32x16& s, float m_use, float& psum, float& qsum,
+  // One slice of the softmax of a half, placed after one MFMA. Each slot holds
+  // independent operations on different terms (scale term k, exp2 of term
+  // k-1, add term k-2 to the sum; later, pack pair j to bf16 and add pair j-1
+  // to the rounded sum), so no slot waits on a transcendental or conversion
+  // result. Every result is tied to its slot by an empty asm: without the tie
+  // the compiler sinks the whole softmax of S_a past the masking branches into
+  // the PV block, where it runs with no MFMA to overlap.
+  auto pin = [](auto& x) { asm volatile("" : "+v"(x)); };
+  uint32_t packed_prev = 0;  // the halves' softmaxes run one after the other, never interleaved
+  auto softmax_step = [&](int k, f32x16& s, float m_use, float& psum, float& qsum,
                           bf16x8* pk) {
-    if (step < 16) {
-      const float p = fast_exp2(__builtin_fmaf(s[step], c2, -m_use));
-      psum += p;
-      s[step] = p;
-    } else if (step < 24) {
-      const int j = step - 16;
-      const bf16x2 b2 = {(__bf16)s[2 * j], (__bf16)s[2 * j + 1]};
-      qsum = __builtin_amdgcn_fdot2_f32_bf16(b2, ones2, qsum, false);
-      pk[j >> 2][2 * (j & 3)] = b2[0];
-      pk[j >> 2][2 * (j & 3) + 1] = b2[1];
+    if (k < 16) {
+      float x = __builtin_fmaf(s[k], c2, -m_use);
+      pin(x);
+      s[k] = x;
+    }
+    if (k >= 1 && k <= 16) {
+      float p = fast_exp2(s[k - 1]);
+      pin(p);
+      s[k - 1] = p;
+    }
+    if (k >= 2 && k <= 17) {
+      psum += s[k - 2];
+      pin(psum);
+    }
+    if (k >= 18 && k < 26) {  // the pair packed in the previous slot
+      qsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed_prev), ones2, qsum, false);
+      pin(qsum);
+    }
+    if (k >= 17 && k < 25) {
+      const int j = k - 17;
+      uint32_t u = pack_bf16x2(s[2 * j], s[2 * j + 1]);
+      pin(u);
+      u32x4 w = __builtin_bit_cast(u32x4, pk[j >> 2]);
+      w[j & 3] = u;
+      pk[j >> 2] = __builtin_bit_cast(bf16x8, w);
+      packed_prev = u;
     }
   };
   auto init_reference = [&](const f32x16& s) {
