@@ -319,6 +319,12 @@ def main():
                     unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4))
     roof["traffic"] = load_traffic(w.spec.name)
     roof["kernel"] = "mla_split_kernel"
+    # The same kernel against what this GPU measurably sustains: a full-load
+    # bf16 MFMA loop (matrix-core bound) or a 256 MiB device copy (HBM bound).
+    ceil = measured_ceilings(dev)
+    measured = ceil["mfma_bf16_TFLOPs"] if roof["bound"] == "mfma" else ceil["copy_GBps"]
+    roof["measured_peak"] = measured
+    roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
 
     value_us = ms_per_step * 1e3
     gbps = wm["total_bytes"] / (value_us * 1e-6) / 1e9
@@ -360,6 +366,45 @@ def main():
         "kernel_source": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_ceilings(dev):
+    """Best-of-5 rates of (a) the library's matrix-core probe, 16 independent
+    bf16 32x32x16 MFMA chains per wave on every CU, and (b) a 256 MiB
+    device-to-device copy (read + write bytes). Both are event-timed on the
+    current stream."""
+    import torch
+
+    import speculative_decode_verify_mla_amd as mv
+
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn, reps=5, warm=2):
+        for _ in range(warm):
+            fn()
+        t = float("inf")
+        for _ in range(reps):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = min(t, e0.elapsed_time(e1) * 1e-3)
+        return t
+
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    iters = 2000
+    flops = float(blocks) * 4 * iters * 16 * 2 * 32 * 32 * 16
+    t_mfma = best(lambda: mv.probe_mfma_bf16(blocks, iters, sink, stream=stream))
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = best(lambda: dst.copy_(src))
+    out = {"mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
+           "copy_GBps": round(2 * src.numel() / t_copy / 1e9, 1)}
+    del src, dst, sink
+    log(f"measured ceilings: {out}")
+    return out
 
 
 def _time_small_op(fn, steps, warmup, dev):

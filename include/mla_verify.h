@@ -243,6 +243,18 @@ size_t mla_select_topk_workspace_bytes(int32_t rows, int32_t row_len);
 /* Static description of an error code (never NULL). */
 const char* mla_verify_strerror(int code);
 
+/* Measurement aid, not a step of the attention path: the bf16 matrix-core rate
+ * this GPU sustains under full load, against which the split kernel's achieved
+ * TFLOP/s can be read next to the published dense peak (clocks under a full
+ * matrix-core load sit well below the peak's). Launches `blocks` workgroups of
+ * 4 waves; every wave runs `iters` rounds of 16 independent
+ * v_mfma_f32_32x32x16_bf16 (32,768 flops each), so one launch performs
+ * blocks x 4 x iters x 16 x 32,768 flops. Each thread writes one float of
+ * `sink` (device memory, at least blocks x 256 floats). Checks
+ * (MLA_ERR_INVALID): 1 <= blocks <= 65,536, 1 <= iters <= 1,000,000, sink
+ * non-NULL and 4-byte aligned. Enqueued on `stream`; time it with events. */
+int mla_probe_mfma_bf16(int32_t blocks, int32_t iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,6 +35,7 @@ EXPORTED = (
     "mla_head_project",
     "mla_select_topk",
     "mla_select_topk_workspace_bytes",
+    "mla_probe_mfma_bf16",
 )
 
 
@@ -107,6 +108,8 @@ def load_library(path: Optional[str] = None):
         lib.mla_select_topk.restype = i32
         lib.mla_select_topk_workspace_bytes.argtypes = [i32, i32]
         lib.mla_select_topk_workspace_bytes.restype = sz
+        lib.mla_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
+        lib.mla_probe_mfma_bf16.restype = i32
         lib.mla_verify_strerror.argtypes = [i32]
         lib.mla_verify_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -267,6 +270,23 @@ def head_project(x, w, y, stream=None):
                                          ctypes.c_void_p(stream.cuda_stream))
     if rc != MLA_OK:
         raise MlaError(rc, "mla_head_project")
+
+
+def probe_mfma_bf16(blocks: int, iters: int, sink, stream=None) -> float:
+    """Enqueue the matrix-core throughput probe (mla_probe_mfma_bf16) and return
+    the flops that launch performs; `sink` is a float32 device tensor of at
+    least blocks x 256 elements."""
+    import torch
+
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 256:
+        raise ValueError("probe_mfma_bf16: sink must be float32 with blocks x 256 elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(sink.device)
+    rc = load_library().mla_probe_mfma_bf16(int(blocks), int(iters), _ptr(sink),
+                                            ctypes.c_void_p(stream.cuda_stream))
+    if rc != MLA_OK:
+        raise MlaError(rc, "mla_probe_mfma_bf16")
+    return float(blocks) * 4 * iters * 16 * 2 * 32 * 32 * 16
 
 
 def topk_workspace_bytes(rows: int, row_len: int) -> int:

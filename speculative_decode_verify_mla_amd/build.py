@@ -11,7 +11,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmla_verify.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mla_api.hip", "mla_kernels.hip", "mla_compact.hip", "mla_proj.hip", "mla_topk.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mla_api.hip", "mla_kernels.hip", "mla_compact.hip", "mla_proj.hip", "mla_topk.hip", "mla_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -367,6 +367,16 @@ int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k
   return MLA_OK;
 }
 
+int mla_probe_mfma_bf16(int32_t blocks, int32_t iters, float* sink, void* stream) {
+  if (blocks < 1 || blocks > 65536 || iters < 1 || iters > 1000000) return MLA_ERR_INVALID;
+  if (!sink || !aligned(sink, 4)) return MLA_ERR_INVALID;
+  const int rc = check_device();
+  if (rc != MLA_OK) return rc;
+  if (mlav::launch_probe_mfma(sink, blocks, iters, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_verify_strerror(int code) {
   switch (code) {
     case MLA_OK: return "success";

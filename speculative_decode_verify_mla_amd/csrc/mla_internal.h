@@ -120,4 +120,7 @@ hipError_t launch_topk_kernel(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_split_kernel(const MainArgs& a, int mode, hipStream_t stream);
 hipError_t launch_combine_kernel(const MainArgs& a, int mode, hipStream_t stream);
 
+// Matrix-core throughput probe (a measurement aid).
+hipError_t launch_probe_mfma(float* sink, int blocks, int iters, hipStream_t stream);
+
 }  // namespace mlav

@@ -94,6 +94,16 @@ __device__ __forceinline__ void score_fence(f32x16& s) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
 }
 
+// Two floats times a scale, each rounded once (to nearest even) to fp16, packed
+// low = x0: the low half written by v_fma_mixlo_f16, the high half by
+// v_fma_mixhi_f16 into the same register (no separate shift and merge).
+__device__ __forceinline__ uint32_t scale_pack_f16x2(float x0, float x1, float s) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %3, 0 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %2, %3, 0 op_sel_hi:[0,0,0]"
+      : "=&v"(r) : "v"(x0), "v"(x1), "v"(s));
+  return r;
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -783,10 +793,8 @@ mla_split_kernel(MainArgs a) {
         for (int qq = 0; qq < 4; ++qq) {
           const int d = db * 32 + 8 * qq + 4 * half;
           uint2 pkd;
-          pkd.x = (uint32_t)bf16_bits(o[db][4 * qq + 0] * inv) |
-                  ((uint32_t)bf16_bits(o[db][4 * qq + 1] * inv) << 16);
-          pkd.y = (uint32_t)bf16_bits(o[db][4 * qq + 2] * inv) |
-                  ((uint32_t)bf16_bits(o[db][4 * qq + 3] * inv) << 16);
+          pkd.x = pack_bf16x2(o[db][4 * qq + 0] * inv, o[db][4 * qq + 1] * inv);
+          pkd.y = pack_bf16x2(o[db][4 * qq + 2] * inv, o[db][4 * qq + 3] * inv);
           *reinterpret_cast<uint2*>(dst + d) = pkd;
         }
       }
@@ -811,11 +819,9 @@ mla_split_kernel(MainArgs a) {
     for (int db = 0; db < 16; ++db) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const _Float16 h0 = (_Float16)(o[db][4 * qq + 0] * inv_s), h1 = (_Float16)(o[db][4 * qq + 1] * inv_s);
-        const _Float16 h2 = (_Float16)(o[db][4 * qq + 2] * inv_s), h3 = (_Float16)(o[db][4 * qq + 3] * inv_s);
         uint2 pkd;
-        pkd.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        pkd.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+        pkd.x = scale_pack_f16x2(o[db][4 * qq + 0], o[db][4 * qq + 1], inv_s);
+        pkd.y = scale_pack_f16x2(o[db][4 * qq + 2], o[db][4 * qq + 3], inv_s);
         *reinterpret_cast<uint2*>(dst + ((db * 4 + qq) * 64 + lane) * 4) = pkd;
       }
     }

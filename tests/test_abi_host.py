@@ -224,3 +224,10 @@ def test_topk_workspace_bytes(lib):
     assert w(1, 4096) == 0          # one piece: no workspace
     assert w(3, 9000) == 3 * 3 * 1056 + 3 * (9000 + 3 * 1024) * 8
     assert w(0, 100) == 0 and w(2, 0) == 0
+
+
+def test_probe_invalid_arguments(lib):
+    sink = ctypes.c_void_p(0x10000)
+    for blocks, iters, s in ((0, 1, sink), (65537, 1, sink), (1, 0, sink), (1, 1000001, sink),
+                             (1, 1, None), (1, 1, ctypes.c_void_p(0x10002))):
+        assert lib.mla_probe_mfma_bf16(blocks, iters, s, None) == B.MLA_ERR_INVALID
