@@ -262,6 +262,17 @@ def main():
     ms_per_step = t_start.elapsed_time(t_end) / K
     log(f"timed {K} calls: {ms_per_step*1e3:.2f} us/call (cold-rotated)")
 
+    # ---- per-call spread (events around each call, outside the timed region) -----------
+    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        evc[i][0].record(stream)
+        call(copies[i % len(copies)])
+        evc[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in evc]))
+    pct = {f"p{q}": round(float(np.percentile(per_call, q)), 3) for q in (10, 50, 90)}
+    log(f"per-call us: {pct}")
+
     # ---- warm (one copy, Infinity-Cache resident) for context ----------------------------
     t_start.record(stream)
     for i in range(K):
@@ -355,6 +366,7 @@ def main():
                    "workgroups": workgroups},
         "achieved_hbm_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        "per_call_us": pct,
         "warm_us_per_call": round(warm_us, 3),
         "graph_us_per_call": round(graph_us, 3),
         "split_kernel_us": round(split_ms * 1e3, 3),
@@ -364,8 +376,17 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernel_source": kernel_source_hash(),
+        "device": device_info(dev),
     }
     print(json.dumps(line), flush=True)
+
+
+def device_info(dev):
+    import torch
+
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "hbm_GiB": round(p.total_memory / 2**30, 1), "hip": torch.version.hip}
 
 
 def measured_ceilings(dev):
