@@ -286,3 +286,22 @@ def test_ragged_batch_equals_single_sequences(gpu_lib):
         o1, l1 = ds.results()
         assert np.abs(l1[0] - lse[b]).max() < 2e-4
         assert np.abs(o1[0] - out[b]).max() <= OUT_TOL
+
+
+@pytest.mark.parametrize("layout", ["contig", "paged"])
+def test_batch_wider_than_a_wave(gpu_lib, layout):
+    """More sequences than a wave has lanes (80 > 64): the device split plan
+    scans the batch lane-strided; ragged lengths, including an empty prefix and
+    prefixes shorter and longer than one tile, all match the oracle."""
+    rng = np.random.default_rng(21)
+    prefix = [int(x) for x in rng.integers(0, 600, size=80)]
+    prefix[3] = 0
+    prefix[70] = 2500  # one long sequence among many short ones
+    spec = Spec(f"wide_{layout}", B=80, T=2, H=16, layout=layout, prefix=prefix)
+    w = generate(spec, seed=21)
+    _announce(f"batch of 80, {layout}", w)
+    ref_out, ref_lse = run_oracle(w)
+    d = _dev(w)
+    for splits in (0, 3):
+        d.run(num_splits=splits)
+        _check(*d.results(), ref_out, ref_lse, tag=f"wide {layout} s={splits}")
