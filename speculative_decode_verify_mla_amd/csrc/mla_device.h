@@ -13,9 +13,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -59,20 +57,11 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Two floats -> two packed halves (low = a) in one conversion, round to nearest even
-// (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+// Two floats -> two packed bf16 (low = a) in one conversion, round to nearest
+// even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-}
-
-__device__ __forceinline__ uint16_t bf16_bits(float x) {
-  __bf16 h = (__bf16)x;  // v_cvt_pk_bf16_f32: round to nearest even
-  return __builtin_bit_cast(uint16_t, h);
 }
 
 }  // namespace mlav
