@@ -113,7 +113,19 @@ def cpu_baseline(w, budget_s: float):
     return dict(value=per_call_us, unit="us/call", cores=int(threads), kind="oracle",
                 sample=f"{done} (sequence, draft-token) groups of {w.H} heads each, cycling "
                        f"through the call's {len(tokens)}, fp64 numpy oracle, {el:.1f} s wall; "
-                       f"scaled to one whole call")
+                       f"scaled to one whole call",
+                cpu_model=_cpu_model())
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _rows_of(w, b):
