@@ -652,17 +652,18 @@ mla_split_kernel(MainArgs a) {
 
     for (int tile = t_begin; tile < t_end; ++tile) {
       const int stage = (tile - t_begin) & 1;
+      // The next tile's loads (past the split's end: none that touch memory).
+      // Dense: their descriptors depend only on the tile index, so they are built
+      // before the wait, off the path from the barrier to the first MFMA.
+      TileLoad nl;
+      if (!kSparseMode) nl = prepare_dense(tile + 1, stage ^ 1, nv_next);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads (tile data, prefetched indices) landed
       __syncthreads();                // ... and every other wave's; previous stage is free
-      // The next tile's loads (past the split's end: none that touch memory).
-      TileLoad nl;
       if (kSparseMode) {
         const int r1 = tile + 1 < t_end ? resolve_row(idx_next) : -1;
         vm_next = __ballot(r1 >= 0);
         nl = prepare_sparse(r1, stage ^ 1);
         if (tile + 2 < t_end) idx_next = fetch_index(tile + 2);
-      } else {
-        nl = prepare_dense(tile + 1, stage ^ 1, nv_next);
       }
       if (!wave_active) {
 #pragma unroll
