@@ -712,6 +712,10 @@ mla_split_kernel(MainArgs a) {
         bf16x8 ring[kFragAhead];
 #pragma unroll
         for (int j = 0; j < kFragAhead; ++j) ring[j] = frag(j);
+        // Dense: both reads go out before the first MFMA (left alone, the scheduler
+        // issues the second after it, exposing a second LDS round trip per tile).
+        // The sparse modes keep the scheduler's order: the pin costs them spills.
+        if constexpr (!kSparseMode) __builtin_amdgcn_sched_barrier(0);
         // S_a: scores of keys 0..31
         f32x16 sa;
 #pragma unroll
