@@ -694,7 +694,11 @@ mla_split_kernel(MainArgs a) {
         // starts on an LDS round trip. The VALU work is written between the
         // MFMAs: the next tile's loads in S_a, S_a's softmax in S_b, S_b's in PV.
         unsigned kbase = kbaseA, vb0 = vbase[0], vb1 = vbase[1];
-        asm volatile("" : "+v"(kbase), "+v"(vb0), "+v"(vb1));  // see score_chain
+        asm volatile("" : "+v"(vb0), "+v"(vb1));  // see score_chain
+        // Dense: the 8 XOR variants of the K base are hoisted into registers, so
+        // K fragment reads need no address arithmetic; the sparse modes keep them
+        // opaque (hoisting costs them spills).
+        if constexpr (kSparseMode) asm volatile("" : "+v"(kbase));
         auto frag = [&](int f) -> bf16x8 {
           if (f < 72) {
             const int kb = f / 36, c = f % 36;
