@@ -305,3 +305,25 @@ def test_batch_wider_than_a_wave(gpu_lib, layout):
     for splits in (0, 3):
         d.run(num_splits=splits)
         _check(*d.results(), ref_out, ref_lse, tag=f"wide {layout} s={splits}")
+
+
+def test_sparse_leading_padding(gpu_lib):
+    """Sorted index lists whose -1 padding comes first and fills whole 64-key
+    tiles: rows see their first visible key only after several empty tiles (the
+    exponent reference is set mid-split), and with several splits the first
+    ones hold no key at all (weight 0 in the combine)."""
+    spec = Spec("sparse_lead", B=3, T=2, H=64, layout="sparse", cache_len=4000, topk=400)
+    w = generate(spec, seed=23)
+    idx = w.indices.copy()
+    drop = {(0, 0): 150, (0, 1): 330, (1, 0): 64, (2, 1): 399}  # entries replaced by -1
+    for (b, t), n in drop.items():
+        idx[b, t, :n] = -1
+        idx[b, t] = np.sort(idx[b, t])
+    import dataclasses
+    w = dataclasses.replace(w, indices=idx)
+    _announce("sparse with leading padding", w)
+    ref_out, ref_lse = run_oracle(w)
+    d = _dev(w)
+    for splits in (0, 1, 3, 7):
+        d.run(num_splits=splits)
+        _check(*d.results(), ref_out, ref_lse, tag=f"sparse_lead s={splits}")
