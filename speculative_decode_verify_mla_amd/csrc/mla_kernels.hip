@@ -88,9 +88,10 @@ __device__ __forceinline__ f32x16 mfma32_v_first(bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma32_v_acc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-// Independent-instruction wait states between the last score MFMA and any
-// VALU/VMEM/LDS access of its result: 12, the count the compiler itself puts
-// between v_mfma_f32_32x32x16_bf16 and a VALU read of its result on gfx950.
+// Independent-instruction wait states between the last score MFMA and the VALU
+// reads and writes of its result (scores are touched by nothing else): 12, the
+// count the compiler itself puts between v_mfma_f32_32x32x16_bf16 and a VALU
+// read of its result on gfx950.
 __device__ __forceinline__ void score_fence(f32x16& s) {
   asm volatile("s_nop 11" : "+v"(s));
 }
