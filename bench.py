@@ -344,8 +344,24 @@ def main():
     roof["kernel"] = "mla_split_kernel"
     # The same kernel against what this GPU measurably sustains: a full-load
     # bf16 MFMA loop (matrix-core bound) or a 256 MiB device copy (HBM bound).
-    ceil = measured_ceilings(dev)
-    measured = ceil["mfma_bf16_TFLOPs"] if roof["bound"] == "mfma" else ceil["copy_GBps"]
+    gather = None
+    if w.layout == "sparse":
+        # the same rows the call gathers, with no compute, cycling over the same
+        # input copies as the timed calls (so that, like them, it reads from HBM)
+        gsink = torch.empty(w.B * w.T * ((w.topk + 63) // 64) * 256, dtype=torch.float32, device=dev)
+        turn = [0]
+
+        def gather(count=False):
+            c = copies[turn[0] % len(copies)]
+            turn[0] += 1
+            return mv.probe_gather_rows(c["c_kv"], c["k_rope"], idx.reshape(w.B * w.T, -1),
+                                        kv_seq_stride=w.kv_seq_stride, tokens_per_seq=w.T,
+                                        sink=gsink, stream=stream, count=count)
+    ceil = measured_ceilings(dev, gather)
+    if roof["bound"] == "mfma":
+        measured = ceil["mfma_bf16_TFLOPs"]
+    else:
+        measured = ceil.get("gather_GBps", ceil["copy_GBps"])
     roof["measured_peak"] = measured
     roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
 
@@ -386,6 +402,7 @@ def main():
         "algorithmic_bytes": int(wm["total_bytes"]),
         "algorithmic_flops": wm["flops"],
         "roofline": roof,
+        "measured_ceilings": ceil,
         "cpu_baseline": cpu,
         "kernel_source": kernel_source_hash(),
         "device": device_info(dev),
@@ -401,11 +418,12 @@ def device_info(dev):
             "hbm_GiB": round(p.total_memory / 2**30, 1), "hip": torch.version.hip}
 
 
-def measured_ceilings(dev):
+def measured_ceilings(dev, gather=None):
     """Best-of-5 rates of (a) the library's matrix-core probe, 16 independent
-    bf16 32x32x16 MFMA chains per wave on every CU, and (b) a 256 MiB
-    device-to-device copy (read + write bytes). Both are event-timed on the
-    current stream."""
+    bf16 32x32x16 MFMA chains per wave on every CU, (b) a 256 MiB device-to-device
+    copy (read + write bytes) and, when `gather` is given (a call that enqueues the
+    library's row-gather probe, and returns its bytes when called with count=True),
+    (c) that gather. All are event-timed on the current stream."""
     import torch
 
     import speculative_decode_verify_mla_amd as mv
@@ -436,6 +454,9 @@ def measured_ceilings(dev):
     out = {"mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
            "copy_GBps": round(2 * src.numel() / t_copy / 1e9, 1)}
     del src, dst, sink
+    if gather is not None:
+        nbytes = gather(count=True)
+        out["gather_GBps"] = round(nbytes / best(gather) / 1e9, 1)
     log(f"measured ceilings: {out}")
     return out
 

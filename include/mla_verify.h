@@ -255,6 +255,22 @@ const char* mla_verify_strerror(int code);
  * non-NULL and 4-byte aligned. Enqueued on `stream`; time it with events. */
 int mla_probe_mfma_bf16(int32_t blocks, int32_t iters, float* sink, void* stream);
 
+/* Measurement aid, not a step of the attention path: gathers cache rows by index
+ * with no compute, the rate against which the sparse path's gathered bytes can be
+ * read. For group g and k < per_group, index i = indices[g * per_group + k]
+ * selects row (g / tokens_per_seq) * kv_seq_stride + i of c_kv (1,024 bytes) and
+ * of k_rope (128 bytes) when 0 <= i < kv_seq_stride (any i >= 0 when
+ * kv_seq_stride is 0) and the row is below kv_rows; other indices are skipped. One
+ * workgroup of 256 threads per (group, 64 indices), each thread writing one float
+ * of `sink` (at least groups x ceil(per_group / 64) x 256 floats). Checks
+ * (MLA_ERR_INVALID): pointers non-NULL, c_kv and k_rope 16-byte aligned, indices
+ * and sink 4-byte aligned, kv_rows >= 1, 0 <= kv_seq_stride <= 2^21 (kv_rows <=
+ * 2^21 when it is 0), groups, per_group, tokens_per_seq >= 1. Enqueued on
+ * `stream`; time it with events. */
+int mla_probe_gather_rows(const uint16_t* c_kv, const uint16_t* k_rope, int64_t kv_rows,
+                          int64_t kv_seq_stride, const int32_t* indices, int32_t groups,
+                          int32_t per_group, int32_t tokens_per_seq, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

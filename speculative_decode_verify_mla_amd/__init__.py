@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     head_project,
     load_library,
     plan,
+    probe_gather_rows,
     probe_mfma_bf16,
     select_topk,
     topk_workspace_bytes,

@@ -36,6 +36,7 @@ EXPORTED = (
     "mla_select_topk",
     "mla_select_topk_workspace_bytes",
     "mla_probe_mfma_bf16",
+    "mla_probe_gather_rows",
 )
 
 
@@ -110,6 +111,9 @@ def load_library(path: Optional[str] = None):
         lib.mla_select_topk_workspace_bytes.restype = sz
         lib.mla_probe_mfma_bf16.argtypes = [i32, i32, vp, vp]
         lib.mla_probe_mfma_bf16.restype = i32
+        lib.mla_probe_gather_rows.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp, i32, i32,
+                                              i32, vp, vp]
+        lib.mla_probe_gather_rows.restype = i32
         lib.mla_verify_strerror.argtypes = [i32]
         lib.mla_verify_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -287,6 +291,38 @@ def probe_mfma_bf16(blocks: int, iters: int, sink, stream=None) -> float:
     if rc != MLA_OK:
         raise MlaError(rc, "mla_probe_mfma_bf16")
     return float(blocks) * 4 * iters * 16 * 2 * 32 * 32 * 16
+
+
+def probe_gather_rows(c_kv, k_rope, indices, *, kv_seq_stride: int, tokens_per_seq: int, sink,
+                      stream=None, count: bool = True):
+    """Enqueue the row-gather probe (mla_probe_gather_rows) over `indices` [groups,
+    per_group]; with `count`, also return the bytes it gathers (1,152 per index that
+    selects a row; counting synchronises with the device, so timed calls pass
+    count=False). `sink` is a float32 device tensor of at least groups x
+    ceil(per_group / 64) x 256 elements."""
+    import torch
+
+    idx = indices.reshape(indices.shape[0], -1) if indices.dim() != 2 else indices
+    G, K = int(idx.shape[0]), int(idx.shape[1])
+    if sink.dtype != torch.float32 or sink.numel() < G * ((K + 63) // 64) * 256:
+        raise ValueError("probe_gather_rows: sink too small")
+    if stream is None:
+        stream = torch.cuda.current_stream(c_kv.device)
+    rows = int(c_kv.shape[0])
+    rc = load_library().mla_probe_gather_rows(_ptr(_as_u16(c_kv)), _ptr(_as_u16(k_rope)), rows,
+                                              int(kv_seq_stride), _ptr(idx), G, K,
+                                              int(tokens_per_seq), _ptr(sink),
+                                              ctypes.c_void_p(stream.cuda_stream))
+    if rc != MLA_OK:
+        raise MlaError(rc, "mla_probe_gather_rows")
+    if not count:
+        return None
+    base = (torch.arange(G, device=idx.device) // int(tokens_per_seq)) * int(kv_seq_stride)
+    row = idx.to(torch.int64) + base[:, None]
+    valid = (idx >= 0) & (row < rows)
+    if kv_seq_stride > 0:
+        valid &= idx < int(kv_seq_stride)
+    return int(valid.sum().item()) * 1152
 
 
 def topk_workspace_bytes(rows: int, row_len: int) -> int:

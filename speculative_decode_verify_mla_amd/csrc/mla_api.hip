@@ -377,6 +377,33 @@ int mla_probe_mfma_bf16(int32_t blocks, int32_t iters, float* sink, void* stream
   return MLA_OK;
 }
 
+int mla_probe_gather_rows(const uint16_t* c_kv, const uint16_t* k_rope, int64_t kv_rows,
+                          int64_t kv_seq_stride, const int32_t* indices, int32_t groups,
+                          int32_t per_group, int32_t tokens_per_seq, float* sink, void* stream) {
+  if (!c_kv || !k_rope || !indices || !sink || !aligned(c_kv, 16) || !aligned(k_rope, 16) ||
+      !aligned(indices, 4) || !aligned(sink, 4))
+    return MLA_ERR_INVALID;
+  if (kv_rows < 1 || kv_seq_stride < 0 || groups < 1 || per_group < 1 || tokens_per_seq < 1)
+    return MLA_ERR_INVALID;
+  // byte offsets within one sequence's rows stay below 2^31
+  if ((kv_seq_stride > 0 ? kv_seq_stride : kv_rows) > ((int64_t)1 << 21)) return MLA_ERR_INVALID;
+  if ((int64_t)groups * ((per_group + 63) / 64) > 0x7fffffffLL) return MLA_ERR_INVALID;
+  const int rc = check_device();
+  if (rc != MLA_OK) return rc;
+  mlav::GatherProbeArgs a;
+  a.c_kv = c_kv;
+  a.k_rope = k_rope;
+  a.indices = indices;
+  a.sink = sink;
+  a.kv_seq_stride = kv_seq_stride;
+  a.kv_rows = kv_rows;
+  a.groups = groups;
+  a.per_group = per_group;
+  a.tokens_per_seq = tokens_per_seq;
+  if (mlav::launch_probe_gather(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_verify_strerror(int code) {
   switch (code) {
     case MLA_OK: return "success";

@@ -120,7 +120,16 @@ hipError_t launch_topk_kernel(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_split_kernel(const MainArgs& a, int mode, hipStream_t stream);
 hipError_t launch_combine_kernel(const MainArgs& a, int mode, hipStream_t stream);
 
-// Matrix-core throughput probe (a measurement aid).
+// Matrix-core throughput and row-gather probes (measurement aids).
 hipError_t launch_probe_mfma(float* sink, int blocks, int iters, hipStream_t stream);
+struct GatherProbeArgs {
+  const uint16_t* c_kv;    // [kv_rows, 512] bf16
+  const uint16_t* k_rope;  // [kv_rows, 64] bf16
+  const int32_t* indices;  // [groups, per_group]; row = (g / tokens_per_seq) * kv_seq_stride + index
+  float* sink;             // one float per thread of the launch
+  int64_t kv_seq_stride, kv_rows;
+  int32_t groups, per_group, tokens_per_seq;
+};
+hipError_t launch_probe_gather(const GatherProbeArgs& a, hipStream_t stream);
 
 }  // namespace mlav

@@ -231,3 +231,14 @@ def test_probe_invalid_arguments(lib):
     for blocks, iters, s in ((0, 1, sink), (65537, 1, sink), (1, 0, sink), (1, 1000001, sink),
                              (1, 1, None), (1, 1, ctypes.c_void_p(0x10002))):
         assert lib.mla_probe_mfma_bf16(blocks, iters, s, None) == B.MLA_ERR_INVALID
+
+
+def test_gather_probe_invalid_arguments(lib):
+    P16 = ctypes.c_void_p(0x10000)
+    ok = dict(c=P16, r=P16, rows=100, stride=10, idx=P16, g=2, k=64, t=1, s=P16)
+    for bad in (dict(c=None), dict(r=ctypes.c_void_p(0x10008)), dict(idx=ctypes.c_void_p(0x10002)),
+                dict(s=None), dict(rows=0), dict(stride=-1), dict(g=0), dict(k=0), dict(t=0)):
+        a = {**ok, **bad}
+        rc = lib.mla_probe_gather_rows(a["c"], a["r"], a["rows"], a["stride"], a["idx"], a["g"], a["k"],
+                                       a["t"], a["s"], None)
+        assert rc == B.MLA_ERR_INVALID, bad

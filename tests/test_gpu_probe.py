@@ -24,3 +24,59 @@ def test_probe_runs_scales_and_repeats(gpu_lib):
     assert s1.abs().max() > 0
     assert torch.allclose(s4, 4 * s1, rtol=1e-4, atol=1e-2)
     assert torch.equal(again, s1)
+
+
+@pytest.mark.gpu
+def test_gather_probe_reads_the_indexed_rows(gpu_lib):
+    """Each thread of the row-gather probe folds (XOR) the words it loaded: 16 B of
+    each of its wave's 16 latent rows, and for lanes 0..7 words 0 and 3 of 16 B of
+    the rope row. The result is checked word for word against the same fold on the
+    host, with skipped indices (-1, past the sequence or the cache) contributing
+    nothing."""
+    import numpy as np
+
+    mv = gpu_lib
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(5)
+    seqs, stride, T, K = 2, 300, 2, 70           # groups = seqs x T, two 64-index chunks each
+    rows = seqs * stride
+    lat = rng.integers(0, 2**16, size=(rows, 512), dtype=np.uint16)
+    rope = rng.integers(0, 2**16, size=(rows, 64), dtype=np.uint16)
+    idx = rng.integers(0, stride, size=(seqs * T, K)).astype(np.int32)
+    idx[0, :5] = -1
+    idx[3, 7] = 10**6  # past the sequence and the cache: skipped
+    idx[1, 9] = stride + 3  # past its sequence (a row of the next one): skipped
+    G = seqs * T
+    chunks = (K + 63) // 64
+    sink = torch.zeros(G * chunks * 256, dtype=torch.float32, device=dev)
+    c_kv = torch.from_numpy(lat.view(np.int16)).to(dev)
+    k_rope = torch.from_numpy(rope.view(np.int16)).to(dev)
+    nbytes = mv.probe_gather_rows(c_kv, k_rope, torch.from_numpy(idx).to(dev),
+                                  kv_seq_stride=stride, tokens_per_seq=T, sink=sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    lat32, rope32 = lat.view(np.uint32), rope.view(np.uint32)  # [rows, 256], [rows, 32]
+    want = np.zeros_like(got)
+    valid = 0
+    for g in range(G):
+        for c in range(chunks):
+            for t in range(256):
+                w, l = t // 64, t % 64
+                x = np.uint32(0)
+                for i in range(16):
+                    k = c * 64 + w * 16 + i
+                    if k >= K:
+                        continue
+                    row = (g // T) * stride + int(idx[g, k])
+                    if idx[g, k] < 0 or idx[g, k] >= stride or row >= rows:
+                        continue
+                    x ^= np.bitwise_xor.reduce(lat32[row, 4 * l:4 * l + 4])
+                    if l < 8:
+                        x ^= rope32[row, 4 * l] ^ rope32[row, 4 * l + 3]
+                want[(g * chunks + c) * 256 + t] = x
+    for g in range(G):
+        for k in range(K):
+            row = (g // T) * stride + int(idx[g, k])
+            valid += idx[g, k] >= 0 and idx[g, k] < stride and row < rows
+    assert nbytes == valid * 1152
+    assert np.array_equal(got, want)
