@@ -342,8 +342,9 @@ def main():
                     unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4))
     roof["traffic"] = load_traffic(w.spec.name)
     roof["kernel"] = "mla_split_kernel"
-    # The same kernel against what this GPU measurably sustains: a full-load
-    # bf16 MFMA loop (matrix-core bound) or a 256 MiB device copy (HBM bound).
+    # The same kernel against what this GPU measurably sustains: a full-load bf16
+    # MFMA loop (matrix-core bound), or for HBM-bound calls the same rows gathered
+    # with no compute (sparse) or else a 256 MiB device copy.
     gather = None
     if w.layout == "sparse":
         # the same rows the call gathers, with no compute, cycling over the same
