@@ -77,18 +77,12 @@ def work_model(w):
 
 
 # ---------------------------------------------------------------------------
-def cpu_baseline(w, budget_s: float):
-    """Time the fp64 oracle (as it stands) on a bounded sample of the same call."""
-    import numpy as np
-
+def _oracle_sample(w, budget_s: float):
+    """(groups done, wall seconds) of the fp64 oracle cycling over the call's
+    (sequence, draft-token) groups for about budget_s seconds."""
     import oracle
     from speculative_decode_verify_mla_amd.synth import bf16_bits_to_f64
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:
-        threads = os.cpu_count()
     q_lat, q_rope = bf16_bits_to_f64(w.q_lat), bf16_bits_to_f64(w.q_rope)
     c_kv, k_rope = bf16_bits_to_f64(w.c_kv), bf16_bits_to_f64(w.k_rope)
     tokens = [(b, t) for b in range(w.B) for t in range(w.T)]
@@ -108,16 +102,50 @@ def cpu_baseline(w, budget_s: float):
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    el = time.perf_counter() - t0
-    per_call_us = el / done * len(tokens) * 1e6
-    return dict(value=per_call_us, unit="us/call", cores=int(threads), kind="oracle",
-                sample=f"{done} (sequence, draft-token) groups of {w.H} heads each, cycling "
-                       f"through the call's {len(tokens)}, fp64 numpy oracle, {el:.1f} s wall; "
-                       f"scaled to one whole call",
-                cpu_model=_cpu_model())
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s: float, single_thread: bool = False):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same call,
+    with the BLAS threads it finds; with single_thread, also with one thread."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    ntok = w.B * w.T
+    done, el = _oracle_sample(w, budget_s)
+    res = dict(value=el / done * ntok * 1e6, unit="us/call", cores=int(threads), kind="oracle",
+               sample=f"{done} (sequence, draft-token) groups of {w.H} heads each, cycling "
+                      f"through the call's {ntok}, fp64 numpy oracle, {el:.1f} s wall; "
+                      f"scaled to one whole call",
+               cpu_model=_cpu_model(), host_cpus=os.cpu_count())
+    if single_thread:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                d1, e1 = _oracle_sample(w, min(budget_s, 5.0))
+            res["single_thread_us_per_call"] = e1 / d1 * ntok * 1e6
+            res["single_thread_sample"] = f"{d1} groups, {e1:.1f} s wall, BLAS limited to 1 thread"
+        except Exception as e:  # threadpoolctl missing: say so
+            res["single_thread_us_per_call"] = None
+            res["single_thread_sample"] = f"not measured ({e.__class__.__name__})"
+    return res
 
 
 def _cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                name = line.split(":", 1)[1].strip()
+                if name:
+                    return name
+    except Exception:
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
@@ -156,16 +184,23 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = the headline)")
-    ap.add_argument("--copies", type=int, default=4,
-                    help="input copies cycled through so repeats miss the 256 MB Infinity Cache")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 1..5 (3 = the headline); 6 = the single-token decode "
+                         "diagnostic over the 64k prefix")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="input copies cycled through so repeats miss the 256 MB Infinity Cache "
+                         "(0 = enough for twice its size, at least 4)")
     ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic plan")
+    ap.add_argument("--spike", type=float, default=0.0,
+                    help="workload 3 only: plant, in the last tile of every split, a key scoring "
+                         "this many nats above the rest for every query row (0 = off)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("verify", "compact", "proj", "topk"), default="verify",
+    ap.add_argument("--op", choices=("verify", "compact", "proj", "topk", "sweep"), default="verify",
                     help="verify: the attention call (default); compact: post-verify KV "
                          "compaction; proj: the per-head projections around it; topk: "
-                         "top-k index selection for the sparse path")
+                         "top-k index selection for the sparse path; sweep: the verify call "
+                         "over prefixes 1k..64k at T=16 and T=1")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy (hardware counter scale)")
     args = ap.parse_args()
@@ -180,7 +215,6 @@ def main():
 
     import speculative_decode_verify_mla_amd as mv
     from speculative_decode_verify_mla_amd import synth
-    from speculative_decode_verify_mla_amd.synth import DL, DR
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -206,55 +240,30 @@ def main():
     if args.op == "topk":
         bench_topk(args, dev)
         return
+    if args.op == "sweep":
+        bench_sweep(args, dev)
+        return
 
     w = synth.config(args.config)
+    spiked = None
+    if args.spike > 0:
+        if args.config != 3:
+            raise SystemExit("--spike applies to workload 3 only")
+        w, spiked = plant_spikes(w, args, args.spike)
     wm = work_model(w)
-    log(f"workload {w.spec.name}: B={w.B} T={w.T} H={w.H} kv_lens={w.kv_lens.tolist()[:8]} "
-        f"algorithmic bytes {wm['total_bytes']/1e6:.2f} MB flops {wm['flops']:.4e}")
-
-    def up(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
-
-    # ---- device inputs, several copies -------------------------------------------
-    base = {}
-    base["q_lat"], base["q_rope"] = up(w.q_lat), up(w.q_rope)
-    if w.row_ids is None:
-        base["c_kv"], base["k_rope"] = up(w.c_kv), up(w.k_rope)
-    else:
-        base["c_kv"] = torch.full((w.kv_rows, DL), 0x7FC0, dtype=torch.int16, device=dev)
-        base["k_rope"] = torch.full((w.kv_rows, DR), 0x7FC0, dtype=torch.int16, device=dev)
-        rows = torch.from_numpy(w.row_ids).to(dev)
-        base["c_kv"][rows] = up(w.c_kv)
-        base["k_rope"][rows] = up(w.k_rope)
-    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(max(args.copies, 1) - 1)]
-    kv_lens = torch.from_numpy(w.kv_lens).to(dev)
-    mask = None if w.mask_for_kernel is None else torch.from_numpy(w.tree_mask).to(dev)
-    pt = None if w.page_table is None else torch.from_numpy(w.page_table).to(dev)
-    idx = None if w.indices is None else torch.from_numpy(w.indices).to(dev)
-    out = torch.empty((w.B, w.T, w.H, DL), dtype=torch.int16, device=dev)
-    lse = torch.empty((w.B, w.T, w.H), dtype=torch.float32, device=dev)
-    kw = dict(max_kv_len=w.max_kv_len, kv_seq_stride=w.kv_seq_stride, page_size=w.page_size,
-              num_splits=args.splits)
-    dims = mv.binding._dims_from(base["q_lat"], base["c_kv"], kv_lens, page_table=pt,
-                                 topk=0 if idx is None else idx.shape[2], phase=0, **kw)
-    info = mv.plan(dims, sparse=w.layout == "sparse")
-    ws = torch.empty(max(int(info.workspace_bytes), 16), dtype=torch.uint8, device=dev)
-    # split-kernel grid: row blocks x (group, split) slots; dense slots are shared
-    # out on the device by the actual kv_lens
-    workgroups = int(info.split_slots) * int(info.row_blocks)
-    log(f"plan: split_slots={info.split_slots} (splits={info.num_splits} chunk_tiles={info.chunk_tiles} "
-        f"at max_kv_len) row_blocks={info.row_blocks} groups={info.num_groups} workgroups={workgroups} "
-        f"workspace={info.workspace_bytes/1e6:.1f} MB; inputs x{len(copies)} copies")
-    stream = torch.cuda.current_stream(dev)
-
-    def call(c, phase=mv.binding.PHASE_ALL, st=None):
-        st = stream if st is None else st
-        if w.layout == "sparse":
-            mv.sparse_attn(c["q_lat"], c["q_rope"], c["c_kv"], c["k_rope"], pt, idx, kv_lens,
-                           w.scale, out, lse, workspace=ws, stream=st, phase=phase, **kw)
-        else:
-            mv.verify_attn(c["q_lat"], c["q_rope"], c["c_kv"], c["k_rope"], pt, mask, kv_lens,
-                           w.scale, out, lse, workspace=ws, stream=st, phase=phase, **kw)
+    log(f"workload {w.spec.name}{' (spiked)' if spiked else ''}: B={w.B} T={w.T} H={w.H} "
+        f"kv_lens={w.kv_lens.tolist()[:8]} algorithmic bytes {wm['total_bytes']/1e6:.2f} MB "
+        f"flops {wm['flops']:.4e}")
+    ncopies = args.copies if args.copies > 0 else auto_copies(wm["total_bytes"], 4)
+    vc = VerifyCall(w, dev, ncopies, args.splits)
+    log(f"plan: split_slots={vc.info.split_slots} (splits={vc.info.num_splits} chunk_tiles="
+        f"{vc.info.chunk_tiles} at max_kv_len) row_blocks={vc.info.row_blocks} groups="
+        f"{vc.info.num_groups} workgroups={vc.workgroups} workspace={vc.info.workspace_bytes/1e6:.1f} MB; "
+        f"inputs x{ncopies} copies ({ncopies * wm['total_bytes'] / 1e6:.0f} MB of algorithmic bytes)")
+    stream = vc.stream
+    call = vc.call
+    copies = vc.copies
+    smi_before = smi_snapshot()
 
     # ---- warmup -----------------------------------------------------------------------
     for i in range(args.warmup):
@@ -270,9 +279,15 @@ def main():
     for i in range(K):
         call(copies[i % len(copies)])
     t_end.record(stream)
+    # the shader clock right after the timed calls, from a short matrix-core load
+    # enqueued behind them (no host gap in between)
+    clk = ClockProbe(dev, stream)
+    clk.launch()
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / K
-    log(f"timed {K} calls: {ms_per_step*1e3:.2f} us/call (cold-rotated)")
+    clock_after = clk.read()
+    log(f"timed {K} calls: {ms_per_step*1e3:.2f} us/call (cold-rotated); shader clock right after: "
+        f"{clock_after} GHz")
 
     # ---- per-call spread (events around each call, outside the timed region) -----------
     evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
@@ -313,19 +328,29 @@ def main():
     log(f"graph replay: {graph_us:.2f} us/call ({reps} replays of {len(copies)} calls)")
     del graph
 
-    # ---- per-kernel durations: HIP events around each phase on the launch stream ------------
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # ---- four calls in flight on four streams (own outputs and workspaces) -----------------
+    streams4_us = vc.streams_throughput(4, K)
+    log(f"4 streams: {streams4_us:.2f} us per call ({K} calls dealt over 4 streams)")
+
+    # ---- per-kernel durations: back-to-back launches of each phase between two events -------
+    # on the launch stream (the rotated copies as in the timed region); each average
+    # is one launch's duration plus the gap to the next launch on the same queue
+    t_start.record(stream)
     for i in range(K):
-        c = copies[i % len(copies)]
-        ev[i][0].record(stream)
-        call(c, mv.binding.PHASE_PARTIAL)
-        ev[i][1].record(stream)
-        call(c, mv.binding.PHASE_COMBINE)
-        ev[i][2].record(stream)
+        call(copies[i % len(copies)], mv.binding.PHASE_PARTIAL)
+    t_end.record(stream)
     torch.cuda.synchronize()
-    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    combine_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    log(f"split kernel {split_ms*1e3:.2f} us, combine {combine_ms*1e3:.2f} us (event-timed)")
+    split_ms = t_start.elapsed_time(t_end) / K
+    combine_ms = 0.0
+    if vc.info.workspace_bytes > 0:
+        t_start.record(stream)
+        for i in range(K):
+            call(copies[i % len(copies)], mv.binding.PHASE_COMBINE)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        combine_ms = t_start.elapsed_time(t_end) / K
+    log(f"split kernel {split_ms*1e3:.2f} us, combine {combine_ms*1e3:.2f} us "
+        f"(back-to-back launches, event-timed)")
 
     # ---- roofline of the dominant (split) kernel ------------------------------------------
     t_hbm = wm["total_bytes"] / (PEAK_HBM_GBPS * 1e9)
@@ -340,24 +365,12 @@ def main():
         achieved = split_bytes / split_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS,
                     unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4))
-    roof["traffic"] = load_traffic(w.spec.name)
+    roof["traffic"] = None if spiked else load_traffic(w.spec.name)
     roof["kernel"] = "mla_split_kernel"
     # The same kernel against what this GPU measurably sustains: a full-load bf16
     # MFMA loop (matrix-core bound), or for HBM-bound calls the same rows gathered
     # with no compute (sparse) or else a 256 MiB device copy.
-    gather = None
-    if w.layout == "sparse":
-        # the same rows the call gathers, with no compute, cycling over the same
-        # input copies as the timed calls (so that, like them, it reads from HBM)
-        gsink = torch.empty(w.B * w.T * ((w.topk + 63) // 64) * 256, dtype=torch.float32, device=dev)
-        turn = [0]
-
-        def gather(count=False):
-            c = copies[turn[0] % len(copies)]
-            turn[0] += 1
-            return mv.probe_gather_rows(c["c_kv"], c["k_rope"], idx.reshape(w.B * w.T, -1),
-                                        kv_seq_stride=w.kv_seq_stride, tokens_per_seq=w.T,
-                                        sink=gsink, stream=stream, count=count)
+    gather = vc.gather_probe() if w.layout == "sparse" else None
     ceil = measured_ceilings(dev, gather)
     if roof["bound"] == "mfma":
         measured = ceil["mfma_bf16_TFLOPs"]
@@ -365,6 +378,7 @@ def main():
         measured = ceil.get("gather_GBps", ceil["copy_GBps"])
     roof["measured_peak"] = measured
     roof["frac_of_measured"] = round(roof["achieved"] / measured, 4)
+    smi_after = smi_snapshot()
 
     value_us = ms_per_step * 1e3
     gbps = wm["total_bytes"] / (value_us * 1e-6) / 1e9
@@ -372,8 +386,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the fp64 oracle on the host for ~{args.cpu_budget:.0f} s")
-        cpu = cpu_baseline(w, args.cpu_budget)
+        cpu = cpu_baseline(w, args.cpu_budget, single_thread=args.config in (1, 2))
 
+    name = w.spec.name + (f"_spiked{args.spike:g}" if spiked else "")
     line = {
         "metric": METRIC,
         "value": round(value_us, 3),
@@ -387,27 +402,262 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, random draft tree)",
-        "config": {"workload": w.spec.name, "batch": w.B, "draft_tokens": w.T, "heads": w.H,
+        "config": {"workload": name, "batch": w.B, "draft_tokens": w.T, "heads": w.H,
                    "prefix": (w.kv_lens - w.T).tolist() if w.layout != "sparse" else None,
                    "kv_lens": w.kv_lens.tolist()[:8] if w.B <= 8 else f"{w.B} x {int(w.kv_lens[0])}",
                    "latent_dim": 512, "rope_dim": 64, "layout": w.layout,
-                   "topk": w.topk or None, "split_slots": int(info.split_slots),
-                   "workgroups": workgroups},
+                   "topk": w.topk or None, "split_slots": int(vc.info.split_slots),
+                   "workgroups": vc.workgroups, "input_copies": ncopies,
+                   "spikes": None if not spiked else {"nats": args.spike, "keys": spiked}},
         "achieved_hbm_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "per_call_us": pct,
         "warm_us_per_call": round(warm_us, 3),
         "graph_us_per_call": round(graph_us, 3),
+        "streams4_us_per_call": round(streams4_us, 3),
         "split_kernel_us": round(split_ms * 1e3, 3),
         "combine_kernel_us": round(combine_ms * 1e3, 3),
         "algorithmic_bytes": int(wm["total_bytes"]),
         "algorithmic_flops": wm["flops"],
         "roofline": roof,
         "measured_ceilings": ceil,
+        "clocks": {"shader_GHz_after_timed_calls": clock_after,
+                   "shader_GHz_full_mfma_load": ceil.get("probe_clock_GHz"),
+                   "smi_before": smi_before, "smi_after": smi_after},
         "cpu_baseline": cpu,
         "kernel_source": kernel_source_hash(),
         "device": device_info(dev),
     }
+    print(json.dumps(line), flush=True)
+
+
+MALL_BYTES = 256 * 2**20  # MI355X Infinity Cache
+MAX_COPIES = 128
+
+
+def auto_copies(call_bytes, least):
+    """Input copies whose algorithmic bytes add up to twice the Infinity Cache,
+    so that cycling through them reads from HBM (at least `least`; at most
+    MAX_COPIES, which leaves calls of under 4 MB cache-resident)."""
+    return int(min(MAX_COPIES, max(least, -(-2 * MALL_BYTES // int(call_bytes)))))
+
+
+def plant_spikes(w, args, nats):
+    """Workload 3 with, in the last tile of every split the plan makes, one key
+    scoring `nats` above the rest for every query row (the streaming softmax's
+    worst case: its exponent reference must rise in every split)."""
+    import speculative_decode_verify_mla_amd as mv
+    from speculative_decode_verify_mla_amd import synth
+
+    tiles = -(-int(w.kv_lens[0]) // 64)
+    dims = mv.binding.make_dims(batch=1, num_q=w.T, num_heads=w.H, max_kv_len=w.max_kv_len,
+                                kv_rows=w.kv_rows, kv_seq_stride=w.kv_seq_stride,
+                                num_splits=args.splits)
+    n = int(mv.plan(dims).num_splits)
+    bounds = [s * tiles // n for s in range(n + 1)]  # the even spread of one sequence's tiles
+    return synth.plant_late_spikes(w, bounds, nats)
+
+
+class VerifyCall:
+    """One workload resident on the device in several input copies, with its
+    outputs, workspace and a closure that enqueues one whole call."""
+
+    def __init__(self, w, dev, ncopies, splits):
+        import numpy as np
+        import torch
+
+        import speculative_decode_verify_mla_amd as mv
+        from speculative_decode_verify_mla_amd.synth import DL, DR
+
+        self.w, self.dev, self.mv = w, dev, mv
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+        base = {"q_lat": up(w.q_lat), "q_rope": up(w.q_rope)}
+        if w.row_ids is None:
+            base["c_kv"], base["k_rope"] = up(w.c_kv), up(w.k_rope)
+        else:
+            base["c_kv"] = torch.full((w.kv_rows, DL), 0x7FC0, dtype=torch.int16, device=dev)
+            base["k_rope"] = torch.full((w.kv_rows, DR), 0x7FC0, dtype=torch.int16, device=dev)
+            rows = torch.from_numpy(w.row_ids).to(dev)
+            base["c_kv"][rows] = up(w.c_kv)
+            base["k_rope"][rows] = up(w.k_rope)
+        self.copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(ncopies - 1)]
+        self.kv_lens = torch.from_numpy(w.kv_lens).to(dev)
+        self.mask = None if w.mask_for_kernel is None else torch.from_numpy(w.tree_mask).to(dev)
+        self.pt = None if w.page_table is None else torch.from_numpy(w.page_table).to(dev)
+        self.idx = None if w.indices is None else torch.from_numpy(w.indices).to(dev)
+        self.out = torch.empty((w.B, w.T, w.H, DL), dtype=torch.int16, device=dev)
+        self.lse = torch.empty((w.B, w.T, w.H), dtype=torch.float32, device=dev)
+        self.kw = dict(max_kv_len=w.max_kv_len, kv_seq_stride=w.kv_seq_stride,
+                       page_size=w.page_size, num_splits=splits)
+        dims = mv.binding._dims_from(base["q_lat"], base["c_kv"], self.kv_lens, page_table=self.pt,
+                                     topk=0 if self.idx is None else self.idx.shape[2], phase=0,
+                                     **self.kw)
+        self.info = mv.plan(dims, sparse=w.layout == "sparse")
+        self.ws = self.new_workspace()
+        # split-kernel grid: row blocks x (group, split) slots; dense slots are
+        # shared out on the device by the actual kv_lens
+        self.workgroups = int(self.info.split_slots) * int(self.info.row_blocks)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def new_workspace(self):
+        import torch
+        return torch.empty(max(int(self.info.workspace_bytes), 16), dtype=torch.uint8, device=self.dev)
+
+    def call(self, c, phase=0, st=None, out=None, lse=None, ws=None):
+        mv, w = self.mv, self.w
+        st = self.stream if st is None else st
+        out = self.out if out is None else out
+        lse = self.lse if lse is None else lse
+        ws = self.ws if ws is None else ws
+        if w.layout == "sparse":
+            mv.sparse_attn(c["q_lat"], c["q_rope"], c["c_kv"], c["k_rope"], self.pt, self.idx,
+                           self.kv_lens, w.scale, out, lse, workspace=ws, stream=st, phase=phase,
+                           **self.kw)
+        else:
+            mv.verify_attn(c["q_lat"], c["q_rope"], c["c_kv"], c["k_rope"], self.pt, self.mask,
+                           self.kv_lens, w.scale, out, lse, workspace=ws, stream=st, phase=phase,
+                           **self.kw)
+
+    def streams_throughput(self, n, calls):
+        """µs per call with `calls` whole calls dealt round-robin over n streams
+        (each stream its own outputs and workspace, inputs cycling over the
+        copies), from one event on the launch stream before the first and one
+        after all streams joined it again."""
+        import torch
+
+        streams = [torch.cuda.Stream(self.dev) for _ in range(n)]
+        outs = [torch.empty_like(self.out) for _ in range(n)]
+        lses = [torch.empty_like(self.lse) for _ in range(n)]
+        wss = [self.new_workspace() for _ in range(n)]
+        for k in range(n):  # warm each stream once
+            self.call(self.copies[k % len(self.copies)], st=streams[k], out=outs[k], lse=lses[k],
+                      ws=wss[k])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for s in streams:
+            s.wait_stream(self.stream)
+        for i in range(calls):
+            k = i % n
+            self.call(self.copies[i % len(self.copies)], st=streams[k], out=outs[k], lse=lses[k],
+                      ws=wss[k])
+        for s in streams:
+            self.stream.wait_stream(s)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / calls * 1e3
+
+    def gather_probe(self):
+        """A callable enqueuing the row-gather probe over the call's own rows,
+        cycling over the same input copies as the timed calls (so that, like
+        them, it reads from HBM); with count=True it also returns the bytes."""
+        import torch
+
+        w, mv = self.w, self.mv
+        gsink = torch.empty(w.B * w.T * ((w.topk + 63) // 64) * 256, dtype=torch.float32, device=self.dev)
+        turn = [0]
+
+        def gather(count=False):
+            c = self.copies[turn[0] % len(self.copies)]
+            turn[0] += 1
+            return mv.probe_gather_rows(c["c_kv"], c["k_rope"], self.idx.reshape(w.B * w.T, -1),
+                                        kv_seq_stride=w.kv_seq_stride, tokens_per_seq=w.T,
+                                        sink=gsink, stream=self.stream, count=count)
+        return gather
+
+
+class ClockProbe:
+    """A short launch of the matrix-core probe (one workgroup per CU) whose
+    in-kernel stamps give the shader clock: s_memtime cycles over 100 MHz
+    s_memrealtime ticks."""
+
+    def __init__(self, dev, stream, iters=200):
+        import torch
+
+        self.blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+        self.sink = torch.empty(self.blocks * 256, dtype=torch.float32, device=dev)
+        self.stream, self.iters = stream, iters
+
+    def launch(self):
+        import speculative_decode_verify_mla_amd as mv
+        mv.probe_mfma_bf16(self.blocks, self.iters, self.sink, stream=self.stream)
+
+    def read(self):
+        s = self.sink.view(self.blocks, 256)[:, :2].double().sum(dim=0).tolist()
+        return round(s[0] / s[1] * 0.1, 3) if s[1] > 0 else None
+
+
+def smi_snapshot():
+    """Clocks, power and driver as rocm-smi reports them (JSON), or None."""
+    import subprocess
+
+    try:
+        res = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showdriverversion",
+                              "--showproductname", "--json"],
+                             capture_output=True, text=True, timeout=30)
+        d = json.loads(res.stdout)
+    except Exception:
+        return None
+    keep = {}
+    for card, vals in d.items():
+        if not isinstance(vals, dict):
+            continue
+        keep[card] = {k: v for k, v in vals.items()
+                      if any(x in k.lower() for x in ("clock", "power", "driver", "card series",
+                                                        "card model", "gfx", "sku"))}
+    return keep or None
+
+
+def bench_sweep(args, dev):
+    """The verify call over prefixes 1k .. 64k, at T=16 (random tree) and T=1,
+    H=64, contiguous cache. Beside each figure: the fp32 score row a kernel
+    holding the whole row in LDS would need, (512 + 64 + kv_len) x 4 bytes, and
+    whether it fits one workgroup's 160 KiB of LDS on this GPU ("n/a" past it)."""
+    import numpy as np
+    import torch
+
+    from speculative_decode_verify_mla_amd import synth
+
+    lds = 160 * 1024
+    rows = []
+    for T in (16, 1):
+        for L in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
+            spec = synth.Spec(f"sweep_t{T}_l{L}", B=1, T=T, H=64, layout="contig", prefix=L)
+            w = synth.generate(spec, seed=100 + T)
+            wm = work_model(w)
+            ncopies = auto_copies(wm["total_bytes"], 2)
+            vc = VerifyCall(w, dev, ncopies, 0)
+            for i in range(args.warmup):
+                vc.call(vc.copies[i % ncopies])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(vc.stream)
+            for i in range(args.steps):
+                vc.call(vc.copies[i % ncopies])
+            e1.record(vc.stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / args.steps * 1e3
+            naive = (512 + 64 + int(w.kv_lens[0])) * 4
+            r = {"T": T, "prefix": L, "us_per_call": round(us, 3),
+                 "hbm_GBps": round(wm["total_bytes"] / (us * 1e-6) / 1e9, 1),
+                 "TFLOPs": round(wm["flops"] / (us * 1e-6) / 1e12, 1),
+                 "splits": int(vc.info.num_splits), "workgroups": vc.workgroups,
+                 "naive_score_row_bytes": naive,
+                 "naive_row_in_lds": "fits" if naive <= lds else "n/a"}
+            log(f"sweep T={T:2d} prefix={L:6d}: {us:9.2f} us  {r['hbm_GBps']:7.1f} GB/s  "
+                f"{r['TFLOPs']:7.1f} TFLOP/s  splits={r['splits']}  naive row {naive} B: "
+                f"{r['naive_row_in_lds']}")
+            rows.append(r)
+            del vc
+            torch.cuda.empty_cache()
+    line = {"metric": "verify-attn µs/call over prefix length (H=64; T=16 tree and T=1)",
+            "value": None, "unit": "us/call", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) bf16)", "config": {"workload": "prefix_sweep"},
+            "sweep": rows, "kernel_source": kernel_source_hash()}
     print(json.dumps(line), flush=True)
 
 
@@ -421,10 +671,11 @@ def device_info(dev):
 
 def measured_ceilings(dev, gather=None):
     """Best-of-5 rates of (a) the library's matrix-core probe, 16 independent
-    bf16 32x32x16 MFMA chains per wave on every CU, (b) a 256 MiB device-to-device
-    copy (read + write bytes) and, when `gather` is given (a call that enqueues the
-    library's row-gather probe, and returns its bytes when called with count=True),
-    (c) that gather. All are event-timed on the current stream."""
+    bf16 32x32x16 MFMA chains per wave on every CU (with the shader clock its
+    in-kernel stamps read), (b) a 256 MiB device-to-device copy (read + write
+    bytes) and, when `gather` is given (a call that enqueues the library's
+    row-gather probe, and returns its bytes when called with count=True), (c)
+    that gather. All are event-timed on the current stream."""
     import torch
 
     import speculative_decode_verify_mla_amd as mv
@@ -432,7 +683,7 @@ def measured_ceilings(dev, gather=None):
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def best(fn, reps=5, warm=2):
+    def best(fn, reps=5, warm=2, after=None):
         for _ in range(warm):
             fn()
         t = float("inf")
@@ -442,17 +693,27 @@ def measured_ceilings(dev, gather=None):
             e1.record(stream)
             torch.cuda.synchronize()
             t = min(t, e0.elapsed_time(e1) * 1e-3)
+            if after is not None:
+                after()
         return t
 
     blocks = torch.cuda.get_device_properties(dev).multi_processor_count
     sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     iters = 2000
     flops = float(blocks) * 4 * iters * 16 * 2 * 32 * 32 * 16
-    t_mfma = best(lambda: mv.probe_mfma_bf16(blocks, iters, sink, stream=stream))
+    clocks = []
+
+    def read_clock():
+        s = sink.view(blocks, 256)[:, :2].double().sum(dim=0).tolist()
+        if s[1] > 0:
+            clocks.append(s[0] / s[1] * 0.1)
+
+    t_mfma = best(lambda: mv.probe_mfma_bf16(blocks, iters, sink, stream=stream), after=read_clock)
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     t_copy = best(lambda: dst.copy_(src))
     out = {"mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
+           "probe_clock_GHz": round(max(clocks), 3) if clocks else None,
            "copy_GBps": round(2 * src.numel() / t_copy / 1e9, 1)}
     del src, dst, sink
     if gather is not None:

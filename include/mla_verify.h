@@ -107,16 +107,18 @@ typedef struct mla_dims {
   int64_t kv_seq_stride; /* contiguous: rows between consecutive sequences */
   int64_t kv_rows;       /* rows of the c_kv and k_rope allocations */
   int32_t topk;          /* sparse: index-list length per token (ignored by the dense call) */
-  int32_t num_splits;    /* 0 = automatic; else requested KV splits per query group. The
-                            plan caps it at the tile count and at 256, then evens the
-                            tiles per split (the plan reports the splits used). */
+  int32_t num_splits;    /* 0 = automatic; else requested KV splits per query group, capped
+                            at the group's 64-key tile count and at 256 (the plan reports
+                            the splits used). A single dense sequence spreads its tiles
+                            evenly over exactly that many splits; batches and sparse
+                            calls cut every group into chunks of ceil(tiles / splits). */
   int32_t phase;         /* MLA_PHASE_* */
   int32_t reserved;      /* must be 0 */
 } mla_dims;
 
 typedef struct mla_plan_info {
   int32_t num_splits;     /* KV splits per query group (dense: for a group of max_kv_len keys) */
-  int32_t chunk_tiles;    /* 64-key tiles per split (dense: for a group of max_kv_len keys) */
+  int32_t chunk_tiles;    /* most 64-key tiles in one split (dense: for a group of max_kv_len keys) */
   int32_t row_blocks;     /* 128-row blocks per query group */
   int32_t num_groups;     /* query groups: B (dense) or B*T (sparse) */
   int32_t rows_per_group; /* T*H (dense) or H (sparse) */
@@ -126,8 +128,9 @@ typedef struct mla_plan_info {
 } mla_plan_info;
 
 /* Work decomposition of a call with these dims (sparse != 0: mla_sparse_attn).
- * Pure host arithmetic plus a one-time device-attribute query; no device
- * memory is touched. Returns MLA_ERR_INVALID for dims the call would reject. */
+ * A pure function of the dims: host arithmetic only, no HIP call, planned for
+ * gfx950's 256 compute units whatever device is current. Returns
+ * MLA_ERR_INVALID for dims the call would reject. */
 int mla_verify_plan(const mla_dims* dims, int sparse, mla_plan_info* plan);
 
 /* Convenience: mla_verify_plan(...).workspace_bytes, or 0 on invalid dims. */
@@ -242,34 +245,6 @@ size_t mla_select_topk_workspace_bytes(int32_t rows, int32_t row_len);
 
 /* Static description of an error code (never NULL). */
 const char* mla_verify_strerror(int code);
-
-/* Measurement aid, not a step of the attention path: the bf16 matrix-core rate
- * this GPU sustains under full load, against which the split kernel's achieved
- * TFLOP/s can be read next to the published dense peak (clocks under a full
- * matrix-core load sit well below the peak's). Launches `blocks` workgroups of
- * 4 waves; every wave runs `iters` rounds of 16 independent
- * v_mfma_f32_32x32x16_bf16 (32,768 flops each), so one launch performs
- * blocks x 4 x iters x 16 x 32,768 flops. Each thread writes one float of
- * `sink` (device memory, at least blocks x 256 floats). Checks
- * (MLA_ERR_INVALID): 1 <= blocks <= 65,536, 1 <= iters <= 1,000,000, sink
- * non-NULL and 4-byte aligned. Enqueued on `stream`; time it with events. */
-int mla_probe_mfma_bf16(int32_t blocks, int32_t iters, float* sink, void* stream);
-
-/* Measurement aid, not a step of the attention path: gathers cache rows by index
- * with no compute, the rate against which the sparse path's gathered bytes can be
- * read. For group g and k < per_group, index i = indices[g * per_group + k]
- * selects row (g / tokens_per_seq) * kv_seq_stride + i of c_kv (1,024 bytes) and
- * of k_rope (128 bytes) when 0 <= i < kv_seq_stride (any i >= 0 when
- * kv_seq_stride is 0) and the row is below kv_rows; other indices are skipped. One
- * workgroup of 256 threads per (group, 64 indices), each thread writing one float
- * of `sink` (at least groups x ceil(per_group / 64) x 256 floats). Checks
- * (MLA_ERR_INVALID): pointers non-NULL, c_kv and k_rope 16-byte aligned, indices
- * and sink 4-byte aligned, kv_rows >= 1, 0 <= kv_seq_stride <= 2^21 (kv_rows <=
- * 2^21 when it is 0), groups, per_group, tokens_per_seq >= 1. Enqueued on
- * `stream`; time it with events. */
-int mla_probe_gather_rows(const uint16_t* c_kv, const uint16_t* k_rope, int64_t kv_rows,
-                          int64_t kv_seq_stride, const int32_t* indices, int32_t groups,
-                          int32_t per_group, int32_t tokens_per_seq, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

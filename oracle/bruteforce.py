@@ -42,7 +42,8 @@ def verify(q_lat, q_rope, lookup, kv_lens, T, tree_mask=None, indices=None, scal
     """Brute-force verify (dense when ``indices`` is None, sparse otherwise).
 
     ``lookup(b, p)`` returns (c_kv row, k_rope row) for logical position p of
-    sequence b. Returns nested lists out[b][t][h][d] and lse[b][t][h].
+    sequence b, or None when that key's row does not exist (the key is then not
+    attended). Returns nested lists out[b][t][h][d] and lse[b][t][h].
     """
     B = len(q_lat)
     out, lse = [], []
@@ -53,7 +54,7 @@ def verify(q_lat, q_rope, lookup, kv_lens, T, tree_mask=None, indices=None, scal
                 pos = visible(int(kv_lens[b]), T, t, None if tree_mask is None else tree_mask[b][t])
             else:
                 pos = [int(i) for i in indices[b][t] if 0 <= int(i) < int(kv_lens[b])]
-            rows = [lookup(b, p) for p in pos]
+            rows = [r for r in (lookup(b, p) for p in pos) if r is not None]
             kl = [r[0] for r in rows]
             kr = [r[1] for r in rows]
             ot, lt = [], []

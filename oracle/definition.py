@@ -20,7 +20,11 @@ latent):
     lse  = m + ln l                                (natural log)
     out  = sum_p exp(s_p - m) * c_kv[row(p)] / l   (values are the latent rows)
 
-An empty visible set gives out = 0 and lse = -inf.
+An empty visible set gives out = 0 and lse = -inf. A key whose physical row
+lies outside the cache's [0, kv_rows) (a page-table entry that is negative or
+points past the pool) is absent: it leaves the visible set, when kv_rows is
+given (the pages say nothing about invalid pages; this is the plain reading of
+a row that does not exist).
 
 ``attend`` is that definition with one matrix product per side. The same
 result, reached through per-tile running max/sum updates ("Technical Deep
@@ -168,14 +172,23 @@ def _physical_rows(b: int, pos: np.ndarray, kv_seq_stride: int, page_table, page
     return pages * page_size + pos % page_size
 
 
+def _present(rows: np.ndarray, kv_rows):
+    """Mask of the physical rows that exist (all of them when kv_rows is None)."""
+    if kv_rows is None:
+        return np.ones(rows.shape, dtype=bool)
+    return (rows >= 0) & (rows < int(kv_rows))
+
+
 def verify_dense(q_lat, q_rope, c_kv, k_rope, kv_lens, tree_mask, scale: float, *,
-                 kv_seq_stride: int = 0, page_table=None, page_size: int = 0, row_ids=None):
+                 kv_seq_stride: int = 0, page_table=None, page_size: int = 0, row_ids=None,
+                 kv_rows=None):
     """Tree-verify attention for a batch of sequences.
 
     q_lat [B,T,H,512], q_rope [B,T,H,64] (float64); c_kv [rows,512], k_rope [rows,64];
     kv_lens [B] = prefix + T; tree_mask [B,T,T] or None (chain).
     Contiguous caches place sequence b at rows b*kv_seq_stride + p; paged caches
     place logical position p at page_table[b][p // page_size] * page_size + p % page_size.
+    With kv_rows given, keys whose row falls outside [0, kv_rows) are absent.
     Returns out [B,T,H,512], lse [B,T,H].
     """
     B, T, H, _ = q_lat.shape
@@ -186,13 +199,15 @@ def verify_dense(q_lat, q_rope, c_kv, k_rope, kv_lens, tree_mask, scale: float, 
         for t in range(T):
             mrow = None if tree_mask is None else tree_mask[b, t]
             pos = dense_visible_positions(int(kv_lens[b]), T, t, mrow)
-            kl, kr = rows.get(_physical_rows(b, pos, kv_seq_stride, page_table, page_size))
+            phys = _physical_rows(b, pos, kv_seq_stride, page_table, page_size)
+            kl, kr = rows.get(phys[_present(phys, kv_rows)])
             out[b, t], lse[b, t] = attend(q_lat[b, t], q_rope[b, t], kl, kr, scale)
     return out, lse
 
 
 def verify_sparse(q_lat, q_rope, c_kv, k_rope, kv_lens, indices, scale: float, *,
-                  kv_seq_stride: int = 0, page_table=None, page_size: int = 0, row_ids=None):
+                  kv_seq_stride: int = 0, page_table=None, page_size: int = 0, row_ids=None,
+                  kv_rows=None):
     """Sparse top-k attention: query (b, t) sees the positions indices[b, t, :].
 
     Index entries outside [0, kv_lens[b]) select nothing. All heads of a token
@@ -206,6 +221,7 @@ def verify_sparse(q_lat, q_rope, c_kv, k_rope, kv_lens, indices, scale: float, *
         for t in range(T):
             idx = np.asarray(indices[b, t], dtype=np.int64)
             idx = idx[(idx >= 0) & (idx < int(kv_lens[b]))]
-            kl, kr = rows.get(_physical_rows(b, idx, kv_seq_stride, page_table, page_size))
+            phys = _physical_rows(b, idx, kv_seq_stride, page_table, page_size)
+            kl, kr = rows.get(phys[_present(phys, kv_rows)])
             out[b, t], lse[b, t] = attend(q_lat[b, t], q_rope[b, t], kl, kr, scale)
     return out, lse

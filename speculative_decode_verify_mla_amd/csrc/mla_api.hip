@@ -12,6 +12,7 @@
 
 #include "mla_internal.h"
 #include "mla_verify.h"
+#include "mla_verify_probe.h"
 
 namespace {
 
@@ -20,9 +21,8 @@ using mlav::kTile;
 using mlav::kWaves;
 
 constexpr int kMaxDevices = 64;
-// Per-device cache: 0 = unknown, 1 = gfx950, -1 = other. CU count alongside.
+// Per-device cache: 0 = unknown, 1 = gfx950, -1 = other.
 std::atomic<int> g_arch_state[kMaxDevices];
-std::atomic<int> g_cu_count[kMaxDevices];
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -57,18 +57,10 @@ int check_dims(const mla_dims* d, bool sparse, bool paged) {
   return MLA_OK;
 }
 
-// CU count of the current device (256 when it cannot be queried: planning only).
-int device_cus() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  int c = g_cu_count[dev].load(std::memory_order_relaxed);
-  if (c > 0) return c;
-  int v = 0;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-    return 256;
-  g_cu_count[dev].store(v, std::memory_order_relaxed);
-  return v;
-}
+// Compute units the plans are made for: gfx950 (MI355X) has 256. The plans are
+// pure functions of their arguments (no device query), so a workspace size
+// never depends on which device happens to be current.
+constexpr int kPlanCUs = 256;
 
 // Pieces per row for top-k selection: enough (row, piece) workgroups for about
 // two per CU, at most kTopkMaxChunks pieces of at least kTopkMinChunk scores,
@@ -117,7 +109,7 @@ int make_plan(const mla_dims* d, bool sparse, mla_plan_info* p) {
   if (sparse) {
     // Every token has the same number of index tiles: uniform splits.
     splits = d->num_splits > 0 ? d->num_splits
-                               : std::max<int64_t>(1, std::min(device_cus() / (groups * row_blocks), cap));
+                               : std::max<int64_t>(1, std::min(kPlanCUs / (groups * row_blocks), cap));
     splits = std::min<int64_t>(std::min<int64_t>(splits, tiles), mlav::kMaxSplits);
     chunk = ceil_div(tiles, splits);
     splits = ceil_div(tiles, chunk);
@@ -125,19 +117,24 @@ int make_plan(const mla_dims* d, bool sparse, mla_plan_info* p) {
   } else {
     // Dense: the host fixes the (sequence, split) slots per row block; the
     // kernels share them out by the sequences' actual lengths (kv_lens lives on
-    // the device). A requested split count fixes the chunk instead.
-    if (d->num_splits > 0) {
+    // the device) and spread each sequence's tiles evenly over its slots.
+    if (groups == 1) {
+      // One sequence: every slot is one of its splits.
+      slots = d->num_splits > 0 ? std::min<int64_t>(std::min<int64_t>(d->num_splits, tiles), mlav::kMaxSplits)
+                                : std::max<int64_t>(1, std::min<int64_t>(kPlanCUs / row_blocks, cap));
+      splits = slots;
+    } else if (d->num_splits > 0) {
+      // A requested split count fixes the chunk every sequence is cut by.
       const int64_t req = std::min<int64_t>(std::min<int64_t>(d->num_splits, tiles), mlav::kMaxSplits);
       fixed_chunk = ceil_div(tiles, req);
       splits = ceil_div(tiles, fixed_chunk);
       slots = groups * splits;
     } else {
-      slots = std::max<int64_t>(groups, std::min(device_cus() / row_blocks, groups * cap));
+      slots = std::max<int64_t>(groups, std::min<int64_t>(kPlanCUs / row_blocks, groups * cap));
       splits = std::max<int64_t>(1, slots / groups);  // as if every sequence had max_kv_len keys
+      splits = ceil_div(tiles, ceil_div(tiles, splits));
     }
     chunk = ceil_div(tiles, splits);
-    splits = ceil_div(tiles, chunk);
-    if (groups == 1) slots = splits;  // one sequence: exactly its evened splits
   }
   const int64_t slot_stride = slots;
   const int64_t grid = sparse ? row_blocks * slots : row_blocks * slot_stride;
@@ -347,7 +344,7 @@ int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k
       (row_lens && !aligned(row_lens, 4)) || (workspace && !aligned(workspace, 16)))
     return MLA_ERR_INVALID;
   int chunk = row_len;
-  const int pieces = workspace ? topk_pieces(rows, row_len, device_cus(), &chunk) : 1;
+  const int pieces = workspace ? topk_pieces(rows, row_len, kPlanCUs, &chunk) : 1;
   if (pieces > 1 && workspace_bytes < (size_t)mlav::topk_workspace_bytes(rows, pieces, chunk))
     return MLA_ERR_WORKSPACE;
   const int rc = check_device();

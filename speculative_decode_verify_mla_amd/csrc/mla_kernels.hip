@@ -243,10 +243,12 @@ __device__ DenseSlot dense_slot(const MainArgs& a, const BatchTiles& bt, int chu
   return r;
 }
 
-// Tiles per split and splits holding keys for a group of t tiles over n slots.
-__device__ __forceinline__ void spread_tiles(int t, int n, int& chunk, int& active) {
-  chunk = t > 0 ? (t + n - 1) / n : 1;
-  active = t > 0 ? (t + chunk - 1) / chunk : 0;
+// Splits holding keys for a dense group of t tiles over n slots: every slot
+// gets at least one tile when there are enough, and split s of `active` covers
+// tiles [s*t/active, (s+1)*t/active), so lengths differ by at most one tile.
+__device__ __forceinline__ int dense_active(int t, int n) { return t > 0 ? min(t, n) : 0; }
+__device__ __forceinline__ int dense_tile_bound(int s, int t, int active) {
+  return active > 0 ? (int)(((int64_t)s * t) / active) : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -271,7 +273,7 @@ mla_split_kernel(MainArgs a) {
   // case, all row blocks of one KV chunk share one XCD's L2. (Padding other
   // strides to a multiple of 8 measured slower for short sequences.)
   const int bid = blockIdx.x;
-  int rb, split, group, chunk, n_active;
+  int rb, split, group, n_active, t_begin, t_end;
   int64_t rec_slot;  // workspace record of (rb, split, group), before the wave index
   if (kSparseMode) {
     const int sg = a.num_splits * a.num_groups;
@@ -279,29 +281,36 @@ mla_split_kernel(MainArgs a) {
     const int rem = bid - rb * sg;
     split = rem / a.num_groups;
     group = rem - split * a.num_groups;
-    chunk = a.chunk_tiles;
-    n_active = min(a.num_splits, (group_info(a, group, true).n_tiles + chunk - 1) / chunk);
+    const int chunk = a.chunk_tiles;
+    const int n_tiles = group_info(a, group, true).n_tiles;
+    n_active = min(a.num_splits, (n_tiles + chunk - 1) / chunk);
+    t_begin = split * chunk;
+    t_end = min(t_begin + chunk, n_tiles);
     rec_slot = ((int64_t)split * a.num_groups + group) * a.row_blocks + rb;
   } else {
     rb = bid / a.slot_stride;
     const int slot = bid - rb * a.slot_stride;
     if (slot >= a.split_slots) return;
+    int n_slots;
     if (a.num_groups == 1) {
-      // One sequence: all slots are its splits, at the host's chunk (no search).
+      // One sequence: all slots are its splits (no search).
       group = 0;
       split = slot;
-      chunk = a.chunk_tiles;
-      n_active = min(a.split_slots, (group_info(a, 0, false).n_tiles + chunk - 1) / chunk);
+      n_slots = a.split_slots;
     } else {
       const BatchTiles bt = batch_tiles(a);
       const DenseSlot ds = dense_slot(a, bt, dense_chunk(a, bt), slot);
       if (ds.group < 0) return;  // slot left over by the plan
       group = ds.group;
       split = ds.split;
-      spread_tiles(group_info(a, group, false).n_tiles, ds.n_slots, chunk, n_active);
-      if (split == 0 && rb == 0 && threadIdx.x == 0 && a.ws_meta != nullptr)
-        a.ws_meta[group] = make_int2(slot, n_active);  // the combine's map to this group's records
+      n_slots = ds.n_slots;
     }
+    const int n_tiles = group_info(a, group, false).n_tiles;
+    n_active = dense_active(n_tiles, n_slots);
+    t_begin = dense_tile_bound(split, n_tiles, n_active);
+    t_end = split < n_active ? dense_tile_bound(split + 1, n_tiles, n_active) : t_begin;
+    if (a.num_groups > 1 && split == 0 && rb == 0 && threadIdx.x == 0 && a.ws_meta != nullptr)
+      a.ws_meta[group] = make_int2(slot, n_active);  // the combine's map to this group's records
     rec_slot = (int64_t)slot * a.row_blocks + rb;
   }
   // One split holding all of a group's keys writes out/lse itself.
@@ -310,8 +319,6 @@ mla_split_kernel(MainArgs a) {
   const GroupInfo gi = group_info(a, group, kSparseMode);
   const int b = gi.b;
   const int kv_len = gi.kv_len;
-  const int t_begin = split * chunk;
-  const int t_end = min(t_begin + chunk, gi.n_tiles);
 
   const int row0 = rb * kRowsPerBlock + wave * kRowsPerWave;
   const bool wave_active = row0 < a.rows_per_group;
@@ -1020,7 +1027,7 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
     int slot0;
     if (a.num_groups == 1) {
       slot0 = 0;
-      n_active = min(a.split_slots, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
+      n_active = dense_active(gi.n_tiles, a.split_slots);
     } else {
       const int2 m = a.ws_meta[group];  // written by the split kernel
       slot0 = m.x;

@@ -7,7 +7,10 @@
 // independent v_mfma_f32_32x32x16_bf16 with accumulators in the AGPR file and
 // fixed bf16 operands of N(0,1)-like magnitude (operand values change the
 // chip's power draw and so its clock; zeros would overstate the rate), then
-// writes one float per thread so nothing is optimised away.
+// writes one float per thread so nothing is optimised away. Threads 0 and 1 of
+// each workgroup instead write the workgroup's elapsed shader-clock cycles
+// (s_memtime) and constant-rate real-time ticks (s_memrealtime, 100 MHz) over
+// its MFMA loop: their ratio is the clock the chip ran at.
 #include <hip/hip_runtime.h>
 
 #include "mla_device.h"
@@ -30,6 +33,8 @@ mla_probe_mfma_kernel(float* sink, int iters) {
   f32x16 acc[kProbeChains];
 #pragma unroll
   for (int j = 0; j < kProbeChains; ++j) acc[j] = f32x16{};
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < kProbeChains; ++j) acc[j] = mfma32(a, b, acc[j]);
@@ -40,6 +45,11 @@ mla_probe_mfma_kernel(float* sink, int iters) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += acc[j][r];
   }
+  // the sums depend on every MFMA, so the stamps below follow the whole loop
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) s = (float)(c1 - c0) + 0.f * s;
+  if (threadIdx.x == 1) s = (float)(r1 - r0) + 0.f * s;
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 

@@ -313,9 +313,33 @@ CONFIGS = {
     # sparse top-k decode over a 131072-token cache
     5: Spec("sparse_b32_h64_k2048_l131072", B=32, T=1, H=64, layout="sparse",
             cache_len=131072, topk=2048),
+    # diagnostic (not one of the five): workload 3 with a single query token, a
+    # plain decode step over the 64k latent prefix, bound by reading the cache
+    6: Spec("decode_t1_h64_l65536", B=1, T=1, H=64, layout="contig", prefix=65536),
 }
 
 
 def config(i: int, poison: bool = False) -> Workload:
-    """Workload ``i`` (1..5), seeded with its own number."""
+    """Workload ``i`` (1..6), seeded with its own number."""
     return generate(CONFIGS[i], seed=i, poison=poison)
+
+
+def plant_late_spikes(w: Workload, split_bounds, nats: float = 40.0) -> Workload:
+    """Give every query row one key per key range that scores about ``nats``
+    above the rest, placed in the last 64-key tile of each range of
+    ``split_bounds`` (tile boundaries [t0 = 0 < t1 < ... < tn]): rope dim 0 of
+    every query is set to 1 and rope dim 0 of the chosen prefix keys to
+    nats / scale (rounded to bf16). Inputs only; a single contiguous sequence."""
+    assert w.layout == "contig" and w.B == 1
+    w.q_rope[..., 0] = f32_to_bf16_bits(np.ones(w.q_rope[..., 0].shape, np.float32))
+    prefix = int(w.kv_lens[0]) - w.T
+    big = f32_to_bf16_bits(np.array([nats / w.scale], np.float32))[0]
+    keys = []
+    for t0, t_end in zip(split_bounds[:-1], split_bounds[1:]):
+        # 5 keys into the range's last tile, or its last prefix key when that
+        # tile holds draft keys only
+        p = min((int(t_end) - 1) * 64 + 5, prefix - 1)
+        if int(t0) * 64 <= p < prefix:
+            w.k_rope[p, 0] = big
+            keys.append(p)
+    return w, keys

@@ -26,11 +26,11 @@ def run_oracle(w: Workload, mask_override=_DEFAULT):
         return oracle.verify_sparse(d["q_lat"], d["q_rope"], d["c_kv"], d["k_rope"], w.kv_lens,
                                     w.indices, w.scale, kv_seq_stride=w.kv_seq_stride,
                                     page_table=w.page_table, page_size=w.page_size,
-                                    row_ids=w.row_ids)
+                                    row_ids=w.row_ids, kv_rows=w.kv_rows)
     return oracle.verify_dense(d["q_lat"], d["q_rope"], d["c_kv"], d["k_rope"], w.kv_lens,
                                mask, w.scale, kv_seq_stride=w.kv_seq_stride,
                                page_table=w.page_table, page_size=w.page_size,
-                               row_ids=w.row_ids)
+                               row_ids=w.row_ids, kv_rows=w.kv_rows)
 
 
 def bf16_round_f64(x: np.ndarray) -> np.ndarray:

@@ -11,7 +11,8 @@ import speculative_decode_verify_mla_amd as mv
 from speculative_decode_verify_mla_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla_verify.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -22,7 +23,7 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mla_\w+)\(", text, re.M)))
 
 
@@ -144,13 +145,61 @@ def test_plan_shapes():
                kv_rows=32 * 131072, kv_seq_stride=131072)
     p5 = mv.plan(d5, sparse=True)
     assert (p5.num_groups, p5.rows_per_group, p5.row_blocks) == (32, 64, 1)
-    # requested splits are honoured when they divide the tiles evenly, else rounded down
+    # a single sequence takes exactly the requested splits (capped at its tiles),
+    # its tiles spread evenly: 10 tiles over 7 splits are 3 x 2 + 4 x 1
     p5b = mv.plan(_dims(num_splits=7, max_kv_len=640, kv_rows=640, kv_seq_stride=640))
-    assert (p5b.num_splits, p5b.chunk_tiles) == (5, 2)
+    assert (p5b.num_splits, p5b.chunk_tiles) == (7, 2)
     p7 = mv.plan(_dims(num_splits=7, max_kv_len=896, kv_rows=896, kv_seq_stride=896))
     assert p7.num_splits == 7 and p7.chunk_tiles == 2
     p8 = mv.plan(_dims(num_splits=50))
     assert p8.num_splits == 3  # 132 keys = 3 tiles
+
+
+def test_plan_single_sequence_fills_every_slot():
+    # Kimi-like verify (65 tiles, 8 row blocks): 32 splits of 2-3 tiles each, so
+    # 256 workgroups, not 22 splits of 3 (176 workgroups)
+    d = _dims(num_q=16, num_heads=64, max_kv_len=4112, kv_rows=4112, kv_seq_stride=4112)
+    p = mv.plan(d)
+    assert (p.row_blocks, p.split_slots, p.num_splits, p.chunk_tiles) == (8, 32, 32, 3)
+    assert p.workspace_bytes == 32 * 8 * 4 * (32 * 512 * 2 + 3 * 32 * 4)
+
+
+def _plan_tuple(d, sparse=False):
+    p = mv.plan(d, sparse=sparse)
+    return (p.num_splits, p.chunk_tiles, p.row_blocks, p.num_groups, p.rows_per_group,
+            p.split_slots, p.workspace_bytes)
+
+
+PLAN_DIMS = [
+    (dict(num_q=16, num_heads=64, max_kv_len=65552, kv_rows=65552, kv_seq_stride=65552), False),
+    (dict(batch=8, num_q=8, num_heads=64, max_kv_len=30186, kv_rows=8 * 30186,
+          kv_seq_stride=30186), False),
+    (dict(batch=32, num_q=1, num_heads=64, topk=2048, max_kv_len=131072,
+          kv_rows=32 * 131072, kv_seq_stride=131072), True),
+]
+
+
+def test_plan_is_a_function_of_dims_only():
+    """The plan (and so the workspace size) makes no HIP call: a process whose
+    HIP runtime sees no device at all plans exactly as this one does."""
+    import json
+    import subprocess
+    import sys
+
+    here = [_plan_tuple(_dims(**kw), sparse=sp) for kw, sp in PLAN_DIMS]
+    code = (
+        "import json, sys; sys.path.insert(0, %r)\n"
+        "from tests.test_abi_host import PLAN_DIMS, _plan_tuple, _dims\n"
+        "print(json.dumps([_plan_tuple(_dims(**kw), sparse=sp) for kw, sp in PLAN_DIMS]))\n"
+    ) % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))),)
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                         timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert json.loads(res.stdout.strip().splitlines()[-1]) == [list(t) for t in here]
+    # and every figure follows from the dims alone (256 compute units)
+    assert here[0][:6] == (32, 33, 8, 1, 1024, 32)
+    assert here[1][5] == 64 and here[2][:6] == (8, 4, 1, 32, 64, 256)
 
 
 def test_plan_ragged_batch_slots():

@@ -1,15 +1,36 @@
 """Serving-style use of the verify call: captured into a HIP graph and replayed,
-and issued on several streams at once. Every replay and every stream's result
-must equal the eager call bit for bit (the kernels are deterministic and the
-call keeps no state between launches)."""
+and issued on several streams at once ("The SMEM Ceiling", section "CUDA Graph
+Capture Safety"; the 4-stream benchmark of "The Shared Memory Ceiling",
+section "The Message: Reasoning Before Deployment"). The eager result of every
+case is checked against the fp64 oracle (max-abs 1e-2 on out, 1e-3 on lse),
+and every replay and every stream's result must equal the eager call bit for
+bit (the kernels are deterministic and the call keeps no state between
+launches)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 from speculative_decode_verify_mla_amd import synth
 from speculative_decode_verify_mla_amd.synth import DL, Spec, generate
+from tests._util import run_oracle
 
 pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+def _check_oracle(out_t, lse_t, w, tag):
+    """The device result (torch tensors) against the oracle for workload w."""
+    out = synth.bf16_bits_to_f64(out_t.cpu().numpy().view(np.uint16))
+    lse = lse_t.cpu().numpy().astype(np.float64)
+    ref_out, ref_lse = run_oracle(w)
+    e_out = float(np.abs(out - ref_out).max())
+    e_lse = float(np.abs(lse - ref_lse).max())
+    print(f"   {tag}: max|dout|={e_out:.3e} max|dlse|={e_lse:.3e}", flush=True)
+    assert e_out <= OUT_TOL and e_lse <= LSE_TOL, (tag, e_out, e_lse)
 
 CASES = [
     ("long_single", lambda: generate(Spec("g1", B=1, T=16, H=64, layout="contig", prefix=6000), seed=31)),
@@ -38,6 +59,7 @@ def test_graph_replay_equals_eager(gpu_lib, name, make):
     ws = d.workspace()
     d.run(workspace=ws)
     ref_out, ref_lse = _snapshot(d)
+    _check_oracle(ref_out, ref_lse, w, f"{name} eager")
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -64,6 +86,8 @@ def test_graph_replay_equals_eager(gpu_lib, name, make):
         out, lse = _snapshot(d)
         assert torch.equal(out, ref_out), f"replay {rep}: out differs"
         assert torch.equal(lse, ref_lse), f"replay {rep}: lse differs"
+        if rep == 0:
+            _check_oracle(out, lse, w, f"{name} replay")
 
 
 def test_streams_equal_eager(gpu_lib):
@@ -83,6 +107,10 @@ def test_streams_equal_eager(gpu_lib):
         refs.append((outs[k].clone(), lses[k].clone()))
         outs[k].zero_()
         lses[k].zero_()
+    # each stream's queries are the heads rolled by k: its own oracle case
+    for k in range(n):
+        wk = dataclasses.replace(w, q_lat=np.roll(w.q_lat, shift=k, axis=2))
+        _check_oracle(*refs[k], wk, f"stream {k} eager")
     streams = [torch.cuda.Stream() for _ in range(n)]
     torch.cuda.synchronize()
     for rep in range(2):
@@ -94,8 +122,53 @@ def test_streams_equal_eager(gpu_lib):
             assert torch.equal(outs[k], refs[k][0]) and torch.equal(lses[k], refs[k][1]), (rep, k)
 
 
+def test_streams_in_a_graph_equal_oracle(gpu_lib):
+    """Four calls on four streams, forked from and joined into one captured
+    graph (own outputs and workspaces), replayed several times with eager work
+    in between; every stream's output matches the oracle and the eager call."""
+    w = generate(Spec("msg", B=1, T=8, H=64, layout="contig", prefix=5000), seed=35)
+    print("[case] four streams captured in one graph", flush=True)
+    d = _dev(w)
+    n = 4
+    qs = [d.q_lat] + [torch.roll(d.q_lat, shifts=k, dims=2).contiguous() for k in range(1, n)]
+    outs = [torch.empty_like(d.out) for _ in range(n)]
+    lses = [torch.empty_like(d.lse) for _ in range(n)]
+    wss = [d.workspace() for _ in range(n)]
+    for k in range(n):
+        d.run(q_lat=qs[k], out=outs[k], lse=lses[k], workspace=wss[k])
+    torch.cuda.synchronize()
+    refs = [(o.clone(), l.clone()) for o, l in zip(outs, lses)]
+    for k in range(n):
+        wk = dataclasses.replace(w, q_lat=np.roll(w.q_lat, shift=k, axis=2))
+        _check_oracle(*refs[k], wk, f"graph stream {k} eager")
+
+    cap = torch.cuda.Stream()
+    streams = [torch.cuda.Stream() for _ in range(n)]
+    cap.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for k in range(n):
+            streams[k].wait_stream(cap)
+            d.run(q_lat=qs[k], out=outs[k], lse=lses[k], workspace=wss[k], stream=streams[k])
+        for k in range(n):
+            cap.wait_stream(streams[k])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in range(n):
+            outs[k].fill_(0x7FC0)
+            lses[k].fill_(float("nan"))
+            wss[k].fill_(0xFF)
+        d.run(q_lat=qs[(rep + 1) % n], out=d.out, lse=d.lse, workspace=wss[0])  # eager work between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(n):
+            assert torch.equal(outs[k], refs[k][0]) and torch.equal(lses[k], refs[k][1]), (rep, k)
+
+
 def test_topk_graph_replay_equals_eager(gpu_lib):
-    """Top-k over row pieces (five launches sharing a workspace) captured into a
+    """Top-k over row pieces (three launches sharing a workspace) captured into a
     graph: every replay, with the workspace and output scribbled over and other
     eager selections in between, equals the eager call."""
     import speculative_decode_verify_mla_amd as mv

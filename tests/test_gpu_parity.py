@@ -76,7 +76,7 @@ def test_small_parity(gpu_lib, spec, splits):
     _check(*d.results(), *ref, tag=spec.name)
 
 
-@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5, 6])
 def test_config_parity(gpu_lib, i):
     w = synth.config(i)
     _announce(f"config{i}", w)
@@ -327,3 +327,74 @@ def test_sparse_leading_padding(gpu_lib):
     for splits in (0, 1, 3, 7):
         d.run(num_splits=splits)
         _check(*d.results(), ref_out, ref_lse, tag=f"sparse_lead s={splits}")
+
+
+def test_absent_pages_and_out_of_range_indices(gpu_lib):
+    """Page-table entries that are negative or point past the pool read as
+    absent keys, and sparse indices at or past kv_lens[b] select nothing; the
+    rows they would have named hold finite values, so a stray read shows."""
+    import dataclasses
+    spec = Spec("bad_pages", B=3, T=4, H=64, layout="paged", prefix=[700, 1500, 300])
+    w = generate(spec, seed=24)
+    pt = w.page_table.copy()
+    pool = w.kv_rows // w.page_size
+    pt[0, 2] = -1
+    pt[1, 5] = pool + 7
+    pt[1, 20] = -1
+    w = dataclasses.replace(w, page_table=pt)
+    _announce("absent pages", w)
+    ref = run_oracle(w)
+    d = _dev(w)
+    for splits in (0, 1, 3):
+        d.run(num_splits=splits)
+        _check(*d.results(), *ref, tag=f"absent pages s={splits}")
+
+    spec = Spec("sparse_short", B=3, T=2, H=64, layout="sparse", cache_len=5000, topk=300)
+    w = generate(spec, seed=25)
+    kv = w.kv_lens.copy()
+    kv[0], kv[2] = 3000, 1234  # indices at or past these select nothing
+    idx = w.indices.copy()
+    idx[1, 0, -5:-1] = [5000, 5001, 7000, 1 << 30]  # past kv_len (5000); the list stays unsorted
+    w = dataclasses.replace(w, kv_lens=kv, indices=idx)
+    _announce("sparse indices past kv_lens", w)
+    ref = run_oracle(w)
+    d = _dev(w)
+    for splits in (0, 1, 3):
+        d.run(num_splits=splits)
+        _check(*d.results(), *ref, tag=f"sparse past kv_len s={splits}")
+
+    spec = Spec("sparse_paged_bad", B=2, T=2, H=64, layout="sparse", cache_len=3000, topk=200,
+                paged_sparse=True)
+    w = generate(spec, seed=26)
+    pt = w.page_table.copy()
+    pt[0, 3] = -1
+    pt[1, 10] = w.kv_rows // w.page_size + 1
+    w = dataclasses.replace(w, page_table=pt)
+    _announce("sparse over absent pages", w)
+    ref = run_oracle(w)
+    d = _dev(w)
+    for splits in (0, 3):
+        d.run(num_splits=splits)
+        _check(*d.results(), *ref, tag=f"sparse absent pages s={splits}")
+
+
+def test_late_spikes_in_every_split_full_size(gpu_lib):
+    """Workload 3 at full size with, in the last tile of every split, a key
+    scoring ~40 nats above the rest for every row: every split's streaming
+    softmax must move its exponent reference, and the result still matches the
+    oracle."""
+    import speculative_decode_verify_mla_amd as mv
+    w = synth.config(3)
+    tiles = -(-int(w.kv_lens[0]) // 64)
+    dims = mv.binding.make_dims(batch=1, num_q=w.T, num_heads=w.H, max_kv_len=w.max_kv_len,
+                                kv_rows=w.kv_rows, kv_seq_stride=w.kv_seq_stride)
+    n = int(mv.plan(dims).num_splits)
+    w, keys = synth.plant_late_spikes(w, [s * tiles // n for s in range(n + 1)], 40.0)
+    assert len(keys) == n
+    _announce("late spikes in every split", w)
+    d = _dev(w)
+    d.run()
+    out, lse = d.results()
+    ref_out, ref_lse = run_oracle(w)
+    _check(out, lse, ref_out, ref_lse, tag="spiked config3")
+    assert ref_lse.min() > 35.0  # the spikes dominate every row

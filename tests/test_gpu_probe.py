@@ -2,7 +2,10 @@
 
 Every thread's sink value is the sum of its 16 accumulators after `iters`
 rounds of one fixed bf16 product, so it is `iters` times the one-round value
-(up to fp32 rounding of the running sums), and it is the same on every run."""
+(up to fp32 rounding of the running sums), and it is the same on every run.
+Threads 0 and 1 of each workgroup hold the loop's shader-clock cycles and
+100 MHz real-time ticks instead; over a long loop their ratio is a clock
+between 0.3 and 3 GHz."""
 import pytest
 import torch
 
@@ -21,9 +24,19 @@ def test_probe_runs_scales_and_repeats(gpu_lib):
     torch.cuda.synchronize()
     assert f1 == blocks * 4 * 16 * 2 * 32 * 32 * 16 and f4 == 4 * f1
     assert torch.isfinite(s1).all() and torch.isfinite(s4).all()
-    assert s1.abs().max() > 0
-    assert torch.allclose(s4, 4 * s1, rtol=1e-4, atol=1e-2)
-    assert torch.equal(again, s1)
+    v1, v4, va = (x.view(blocks, 256)[:, 2:] for x in (s1, s4, again))
+    assert v1.abs().max() > 0
+    assert torch.allclose(v4, 4 * v1, rtol=1e-4, atol=1e-2)
+    assert torch.equal(va, v1)
+    # clock stamps: elapsed cycles and 100 MHz ticks of each workgroup's loop
+    big = torch.full((256 * 256,), float("nan"), device=dev)
+    mv.probe_mfma_bf16(256, 2000, big)
+    torch.cuda.synchronize()
+    st = big.view(256, 256)[:, :2].double()
+    assert (st > 0).all()
+    ghz = float(st[:, 0].sum() / st[:, 1].sum()) * 0.1
+    print(f"probe clock under full matrix-core load: {ghz:.3f} GHz", flush=True)
+    assert 0.3 < ghz < 3.0
 
 
 @pytest.mark.gpu

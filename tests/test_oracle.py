@@ -309,3 +309,90 @@ def test_sparse_out_of_range_indices_select_nothing():
                                       row_ids=w.row_ids)
     np.testing.assert_array_equal(out, out2)
     np.testing.assert_array_equal(lse, lse2)
+
+
+def _with_bad_pages(w, bad):
+    """Copy of paged workload w whose page_table entries (b, i) in ``bad`` are
+    replaced: -1 (no page) or a page index past the pool."""
+    import dataclasses
+    pt = w.page_table.copy()
+    pool_pages = w.kv_rows // w.page_size
+    for (b, i), kind in bad.items():
+        pt[b, i] = -1 if kind == "neg" else pool_pages + 3
+    return dataclasses.replace(w, page_table=pt)
+
+
+def test_absent_pages_match_bruteforce():
+    """Keys on a page-table entry that is negative or past the pool are not
+    attended: the oracle against brute force told the same rule per key."""
+    w = generate(Spec("tiny_bad_pages", B=2, T=2, H=2, layout="paged", prefix=[13, 6],
+                      page_size=4), seed=61)
+    w = _with_bad_pages(w, {(0, 1): "neg", (0, 3): "past", (1, 0): "neg"})
+    d = oracle_inputs(w)
+    got_out, got_lse = oracle.verify_dense(d["q_lat"], d["q_rope"], d["c_kv"], d["k_rope"],
+                                           w.kv_lens, w.tree_mask, w.scale,
+                                           page_table=w.page_table, page_size=w.page_size,
+                                           kv_rows=w.kv_rows)
+    c, k = d["c_kv"], d["k_rope"]
+
+    def lookup(b, p):
+        r = int(w.page_table[b][p // w.page_size]) * w.page_size + p % w.page_size
+        if r < 0 or r >= w.kv_rows:
+            return None
+        return c[r].tolist(), k[r].tolist()
+
+    ref_out, ref_lse = bruteforce.verify(d["q_lat"].tolist(), d["q_rope"].tolist(), lookup,
+                                         w.kv_lens, w.T, tree_mask=w.tree_mask, scale=w.scale)
+    assert np.abs(got_out - np.array(ref_out)).max() < 1e-12
+    assert np.abs(got_lse - np.array(ref_lse)).max() < 1e-12
+
+
+def test_absent_prefix_page_equals_sparse_over_the_rest():
+    """A one-token dense call whose second prefix page is absent equals a sparse
+    call over exactly the remaining visible positions (an independent route to
+    the same key set)."""
+    import dataclasses
+    w = generate(Spec("t1_bad_page", B=1, T=1, H=3, layout="paged", prefix=[11], page_size=4),
+                 seed=62)
+    w = _with_bad_pages(w, {(0, 1): "neg"})
+    d = oracle_inputs(w)
+    out_d, lse_d = oracle.verify_dense(d["q_lat"], d["q_rope"], d["c_kv"], d["k_rope"], w.kv_lens,
+                                       w.tree_mask, w.scale, page_table=w.page_table,
+                                       page_size=w.page_size, kv_rows=w.kv_rows)
+    keep = np.array([p for p in range(int(w.kv_lens[0])) if p // 4 != 1], dtype=np.int32)
+    out_s, lse_s = oracle.verify_sparse(d["q_lat"], d["q_rope"], d["c_kv"], d["k_rope"], w.kv_lens,
+                                        keep[None, None, :], w.scale, page_table=w.page_table,
+                                        page_size=w.page_size, kv_rows=w.kv_rows)
+    assert np.abs(out_d - out_s).max() < 1e-12 and np.abs(lse_d - lse_s).max() < 1e-12
+    # and differs from the call that reads all 12 keys
+    full = dataclasses.replace(w, page_table=generate(
+        Spec("t1_bad_page", B=1, T=1, H=3, layout="paged", prefix=[11], page_size=4),
+        seed=62).page_table)
+    assert np.abs(run_oracle(full)[1] - lse_d).max() > 1e-6
+
+
+def test_sparse_absent_rows_are_skipped():
+    """Sparse over a paged cache: an index on an absent page selects nothing,
+    like an index past kv_len; the rest are attended (brute force)."""
+    w = generate(Spec("sp_bad_page", B=1, T=2, H=2, layout="sparse", cache_len=16, topk=6,
+                      paged_sparse=True, page_size=4), seed=63)
+    import dataclasses
+    pt = w.page_table.copy()
+    pt[0, 2] = -1
+    idx = w.indices.copy()
+    idx[0, 1, -1] = 40  # past kv_len
+    w = dataclasses.replace(w, page_table=pt, indices=idx)
+    d = oracle_inputs(w)
+    got_out, got_lse = run_oracle(w)
+    where = {int(r): i for i, r in enumerate(w.row_ids)}
+
+    def lookup(b, p):
+        r = int(pt[b][p // 4]) * 4 + p % 4
+        if r < 0 or r >= w.kv_rows:
+            return None
+        return d["c_kv"][where[r]].tolist(), d["k_rope"][where[r]].tolist()
+
+    ref_out, ref_lse = bruteforce.verify(d["q_lat"].tolist(), d["q_rope"].tolist(), lookup,
+                                         w.kv_lens, w.T, indices=idx.tolist(), scale=w.scale)
+    assert np.abs(got_out - np.array(ref_out)).max() < 1e-12
+    assert np.abs(got_lse - np.array(ref_lse)).max() < 1e-12
