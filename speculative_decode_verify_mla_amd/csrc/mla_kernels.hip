@@ -49,7 +49,13 @@ static_assert(kLdsBytes + 16 <= 163840, "two KV stages must fit one gfx950 CU's 
 constexpr int kLoadsPerStage = kStageBytes / (64 * 16);  // 72 wave-wide 16-byte loads
 static_assert(kLoadsPerStage == 72 && kLoadsPerStage % kWaves == 0, "load split");
 constexpr unsigned kOobOffset = 0x80000000u;     // an offset every range check rejects
-constexpr float kOverflowLog2 = 32.0f;           // largest exponent (log2 units) a term may take
+// Exponent reference bounds (log2 units). A tile whose row sum reaches
+// 2^kRaiseLog2 raises the row's reference at the tile's end (an exact
+// power-of-two rescale); one that reaches 2^kRerunLog2 (a single tile more than
+// ~96 log2 units above the reference, where an fp32 term could overflow) makes
+// the split run again with the reference at that tile's maximum.
+constexpr float kRaiseLog2 = 32.0f;
+constexpr float kRerunLog2 = 96.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 // LDS fragments in flight ahead of the MFMA that consumes them: one wave per
 // SIMD leaves nothing else to cover the LDS latency.
@@ -540,12 +546,16 @@ mla_split_kernel(MainArgs a) {
 
 
   // ---- softmax state ------------------------------------------------------------
-  // The accumulator is never rescaled inside the loop: every exponent is taken
-  // against a fixed per-row reference m_ref (the row max of the first half-tile
-  // with a visible key). A half-tile whose row sum reaches 2^32 (some score more
-  // than 32 log2-units above m_ref) marks the split for a second pass, run with
-  // a reference raised to the largest score seen there, so no term ever exceeds
-  // 2^32 and the result is exact either way.
+  // Exponents are taken against a per-row reference m_ref (log2 units), not a
+  // running max: set at the row max of the first half-tile with a visible key,
+  // it stays put tile after tile while the accumulators stay in place. A tile
+  // whose row sum reaches 2^32 (a score more than ~32 log2 units above m_ref)
+  // raises m_ref at the tile's end by the whole number k = ceil(log2 sum), and
+  // O and the row sums, that tile's terms included, are scaled by 2^-k: exact
+  // in fp32, so the result equals the one the higher reference would have
+  // given throughout. Terms stay below 2^96 inside a tile (fp32 safe); a tile
+  // beyond that (a jump of more than ~96 log2 units) sends the split to a
+  // second pass with the reference at the largest score seen.
   f32x16 o[16];
   float m_ref = -__builtin_inff();   // log2 domain; equal in both lanes of a row
   float m_hi = -__builtin_inff();    // largest score of half-tiles that overflowed
@@ -769,8 +779,42 @@ mla_split_kernel(MainArgs a) {
         l_run += psa + psb;
         lq_run += qsa + qsb;
 
-        // -- rare: a term reached 2^32; find this tile's largest scores -----------
-        const bool ovf = !(psa < 4294967296.0f) || !(psb < 4294967296.0f);
+        // -- rare: the tile's row sum reached 2^kRaiseLog2: raise the reference --
+        const float tsum = psa + psb;
+        if (__ballot(!(tsum < __builtin_ldexpf(1.0f, (int)kRaiseLog2))) != 0ull) {
+          const float row_sum = tsum + __shfl_xor(tsum, 32);
+          // k = ceil(log2(row sum)) whole powers of two (0 for rows that stay)
+          const int k = row_sum >= __builtin_ldexpf(1.0f, (int)kRaiseLog2) && row_sum < __builtin_inff()
+                            ? __builtin_amdgcn_frexp_expf(row_sum) : 0;
+          const float f = __builtin_ldexpf(1.0f, -k);
+          // register by register in place (a plain vector multiply makes the
+          // compiler move the whole accumulator file out of the AGPRs, and spill);
+          // first the wait states between the tile's last MFMA and AGPR reads of
+          // its result, which the compiler cannot see inside the asm
+          asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+          for (int d = 0; d < 16; ++d) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              float x = o[d][e];
+              float tmp;
+              asm volatile(
+                  "v_accvgpr_read_b32 %1, %0\n\t"
+                  "v_mul_f32 %1, %1, %2\n\t"
+                  "v_accvgpr_write_b32 %0, %1"
+                  : "+a"(x), "=&v"(tmp)
+                  : "v"(f));
+              o[d][e] = x;
+            }
+          }
+          l_run *= f;
+          lq_run *= f;
+          m_ref += (float)k;
+        }
+
+        // -- rarer: a tile jumped past 2^kRerunLog2; find its largest scores --------
+        const float rerun_at = __builtin_ldexpf(1.0f, (int)kRerunLog2);
+        const bool ovf = !(psa < rerun_at) || !(psb < rerun_at);
         if (__ballot(ovf) != 0ull) {
           f32x16 ra = score_chain(sb, 0, [](int) {});
           apply_mask(ra, 0);

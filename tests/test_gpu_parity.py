@@ -398,3 +398,23 @@ def test_late_spikes_in_every_split_full_size(gpu_lib):
     ref_out, ref_lse = run_oracle(w)
     _check(out, lse, ref_out, ref_lse, tag="spiked config3")
     assert ref_lse.min() > 35.0  # the spikes dominate every row
+
+
+def test_reference_rises_several_times_in_a_split(gpu_lib):
+    """Keys scoring ~30, ~55 and ~80 nats above the rest at growing positions:
+    each lies more than 2^32 above the exponent reference of the tiles before
+    it, so the reference rises three times within one split (an exact
+    power-of-two rescale of the accumulators each time), and with several
+    splits some rise once; every result matches the oracle."""
+    spec = Spec("three_rises", B=1, T=2, H=64, layout="contig", prefix=3000)
+    w = generate(spec, seed=27)
+    w.q_rope[..., 0] = synth.f32_to_bf16_bits(np.ones(w.q_rope[..., 0].shape, np.float32))
+    for p, nats in ((200, 30.0), (900, 55.0), (2000, 80.0)):
+        w.k_rope[p, 0] = synth.f32_to_bf16_bits(np.array([nats / w.scale], np.float32))[0]
+    _announce("reference rises three times", w)
+    ref_out, ref_lse = run_oracle(w)
+    assert ref_lse.min() > 75.0
+    d = _dev(w)
+    for s in (1, 0, 3):
+        d.run(num_splits=s)
+        _check(*d.results(), ref_out, ref_lse, tag=f"three rises splits={s}")
