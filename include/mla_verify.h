@@ -82,11 +82,15 @@ extern "C" {
 #define MLA_ERR_WORKSPACE (-2)   /* workspace NULL or smaller than the plan's workspace_bytes */
 #define MLA_ERR_HIP (-3)         /* a HIP runtime call or kernel launch failed */
 #define MLA_ERR_UNSUPPORTED (-4) /* the current device is not gfx950 */
+#define MLA_ERR_SCRATCH (-5)     /* mla_verify_attn_noalloc: the call's partials exceed the
+                                    library's fixed device scratch */
 
 #define MLA_LATENT_DIM 512
 #define MLA_ROPE_DIM 64
 #define MLA_MAX_DRAFT 64  /* T limit: one 64-bit visibility word per query row */
 #define MLA_KV_TILE 64    /* keys per LDS tile; page_size must be a multiple */
+/* fixed device scratch behind mla_verify_attn_noalloc (per GPU, process lifetime) */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Which kernels a call enqueues. PARTIAL runs only the split-KV kernel (it
  * writes the per-split partial results into the workspace, or the final
@@ -150,6 +154,26 @@ int mla_verify_attn(const mla_dims* dims, const uint16_t* q_lat, const uint16_t*
                     const uint8_t* tree_mask, const int32_t* kv_lens, float scale,
                     uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Allocation-free variant of mla_verify_attn, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid allocation. Same arguments, checks, operation and
+ * results as mla_verify_attn with a workspace (the same kernels run), but the
+ * split partials live in a fixed device array inside the library instead of a
+ * caller workspace: MLA_NOALLOC_SCRATCH_BYTES bytes (64 MiB), held on
+ * each GPU the library runs on until the process ends. A call whose plan needs
+ * more (mla_verify_plan(...).workspace_bytes larger than that) returns
+ * MLA_ERR_SCRATCH before any HIP call. The first call on each device looks up
+ * that device's copy of the array (a runtime symbol lookup, no allocation by
+ * the library); no call allocates or frees. Every call on one GPU shares the
+ * array, which keeps the last call's contents (the kernels write every record
+ * before reading it, so nothing needs clearing): calls that overlap on one
+ * GPU (other streams, other threads) race and give undefined results. */
+int mla_verify_attn_noalloc(const mla_dims* dims, const uint16_t* q_lat, const uint16_t* q_rope,
+                            const uint16_t* c_kv, const uint16_t* k_rope,
+                            const int32_t* page_table, const uint8_t* tree_mask,
+                            const int32_t* kv_lens, float scale, uint16_t* out, float* lse,
+                            void* stream);
 
 /* Sparse top-k attention: token (b,t) sees indices[b,t,0..topk) (logical
  * positions of sequence b), shared by its H heads; no tree mask. Same checks

@@ -17,5 +17,6 @@ from .binding import (  # noqa: F401
     sparse_attn,
     strerror,
     verify_attn,
+    verify_attn_noalloc,
     workspace_bytes,
 )

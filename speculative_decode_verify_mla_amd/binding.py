@@ -20,6 +20,8 @@ MLA_ERR_INVALID = -1
 MLA_ERR_WORKSPACE = -2
 MLA_ERR_HIP = -3
 MLA_ERR_UNSUPPORTED = -4
+MLA_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_NOALLOC_SCRATCH_BYTES
 
 PHASE_ALL = 0
 PHASE_PARTIAL = 1
@@ -29,6 +31,7 @@ EXPORTED = (
     "mla_verify_plan",
     "mla_verify_workspace_bytes",
     "mla_verify_attn",
+    "mla_verify_attn_noalloc",
     "mla_sparse_attn",
     "mla_verify_strerror",
     "mla_compact_kv",
@@ -101,6 +104,8 @@ def load_library(path: Optional[str] = None):
         lib.mla_verify_attn.restype = i32
         lib.mla_sparse_attn.argtypes = common
         lib.mla_sparse_attn.restype = i32
+        lib.mla_verify_attn_noalloc.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp]
+        lib.mla_verify_attn_noalloc.restype = i32
         lib.mla_compact_kv.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.mla_compact_kv.restype = i32
         lib.mla_head_project.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
@@ -125,7 +130,9 @@ def strerror(code: int) -> str:
         return load_library().mla_verify_strerror(int(code)).decode()
     except Exception:  # library missing: still describe the code
         return {0: "success", -1: "invalid argument", -2: "workspace missing or too small",
-                -3: "HIP runtime or launch failure", -4: "device is not gfx950"}.get(code, "unknown")
+                -3: "HIP runtime or launch failure", -4: "device is not gfx950",
+                -5: "call needs more than the fixed device scratch of the allocation-free "
+                    "entry point"}.get(code, "unknown")
 
 
 def make_dims(*, batch, num_q, num_heads, max_kv_len, kv_rows, kv_seq_stride=0, page_size=0,
@@ -220,6 +227,27 @@ def verify_attn(q_lat, q_rope, c_kv, k_rope, page_table, tree_mask, kv_lens, sca
     _call("mla_verify_attn", dims, False, _as_u16(q_lat), _as_u16(q_rope), _as_u16(c_kv),
           _as_u16(k_rope), page_table, tree_mask, kv_lens, scale, _as_u16(out), lse, workspace,
           stream)
+
+
+def verify_attn_noalloc(q_lat, q_rope, c_kv, k_rope, page_table, tree_mask, kv_lens, scale, out,
+                        lse, *, max_kv_len: int, kv_seq_stride: int = 0, page_size: int = 0,
+                        num_splits: int = 0, phase: int = PHASE_ALL, stream=None):
+    """Dense tree-verify attention without a workspace (mla_verify_attn_noalloc):
+    the split partials use the library's fixed device scratch. Calls on one
+    GPU must not overlap."""
+    import torch
+
+    dims = _dims_from(q_lat, c_kv, kv_lens, max_kv_len=max_kv_len, kv_seq_stride=kv_seq_stride,
+                      page_table=page_table, page_size=page_size, topk=0, num_splits=num_splits,
+                      phase=phase)
+    if stream is None:
+        stream = torch.cuda.current_stream(q_lat.device)
+    rc = load_library().mla_verify_attn_noalloc(
+        ctypes.byref(dims), _ptr(_as_u16(q_lat)), _ptr(_as_u16(q_rope)), _ptr(_as_u16(c_kv)),
+        _ptr(_as_u16(k_rope)), _ptr(page_table), _ptr(tree_mask), _ptr(kv_lens),
+        ctypes.c_float(scale), _ptr(_as_u16(out)), _ptr(lse), ctypes.c_void_p(stream.cuda_stream))
+    if rc != MLA_OK:
+        raise MlaError(rc, "mla_verify_attn_noalloc")
 
 
 def sparse_attn(q_lat, q_rope, c_kv, k_rope, page_table, indices, kv_lens, scale, out, lse, *,

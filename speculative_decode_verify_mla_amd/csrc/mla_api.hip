@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "mla_internal.h"
 #include "mla_verify.h"
@@ -153,10 +154,48 @@ int make_plan(const mla_dims* d, bool sparse, mla_plan_info* p) {
   return MLA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Fixed device scratch of the allocation-free entry point: the split partials
+// of calls that cannot allocate a workspace live here. In host code `scratch`
+// names only a host-side stand-in: its device address on each GPU comes from
+// hipGetSymbolAddress, looked up once per device (with that device current)
+// and kept; only that address ever reaches a kernel. Every call on one GPU
+// shares the array, so calls that overlap on one GPU race.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (first call on a device: looked up
+// and kept). MLA_OK, or MLA_ERR_HIP when the runtime fails.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+        return MLA_ERR_HIP;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MLA_OK;
+}
+
+// `use_scratch`: take the split partials' memory from the fixed device scratch
+// (workspace and workspace_bytes are ignored; a call needing more than
+// kScratchBytes is MLA_ERR_SCRATCH) instead of the caller's workspace.
 int run(const mla_dims* d, bool sparse, const uint16_t* q_lat, const uint16_t* q_rope,
         const uint16_t* c_kv, const uint16_t* k_rope, const int32_t* page_table,
         const uint8_t* tree_mask, const int32_t* indices, const int32_t* kv_lens, float scale,
-        uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+        uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+        bool use_scratch = false) {
   if (d == nullptr) return MLA_ERR_INVALID;
   // a page table and a page size come together, or neither does
   if ((page_table != nullptr) != (d->page_size != 0)) return MLA_ERR_INVALID;
@@ -174,12 +213,18 @@ int run(const mla_dims* d, bool sparse, const uint16_t* q_lat, const uint16_t* q
   mla_plan_info p;
   rc = make_plan(d, sparse, &p);
   if (rc != MLA_OK) return rc;
-  if (p.workspace_bytes > 0) {
+  if (use_scratch) {
+    if (p.workspace_bytes > kScratchBytes) return MLA_ERR_SCRATCH;
+  } else if (p.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < p.workspace_bytes || !aligned(workspace, 16))
       return MLA_ERR_WORKSPACE;
   }
   rc = check_device();
   if (rc != MLA_OK) return rc;
+  if (use_scratch && p.workspace_bytes > 0) {
+    rc = scratch_address(&workspace);
+    if (rc != MLA_OK) return rc;
+  }
 
   mlav::MainArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -266,6 +311,15 @@ int mla_sparse_attn(const mla_dims* dims, const uint16_t* q_lat, const uint16_t*
                     void* stream) {
   return run(dims, true, q_lat, q_rope, c_kv, k_rope, page_table, nullptr, indices, kv_lens,
              scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_verify_attn_noalloc(const mla_dims* dims, const uint16_t* q_lat, const uint16_t* q_rope,
+                            const uint16_t* c_kv, const uint16_t* k_rope,
+                            const int32_t* page_table, const uint8_t* tree_mask,
+                            const int32_t* kv_lens, float scale, uint16_t* out, float* lse,
+                            void* stream) {
+  return run(dims, false, q_lat, q_rope, c_kv, k_rope, page_table, tree_mask, nullptr, kv_lens,
+             scale, out, lse, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 int mla_compact_kv(const mla_dims* dims, uint16_t* c_kv, uint16_t* k_rope,
@@ -408,6 +462,7 @@ const char* mla_verify_strerror(int code) {
     case MLA_ERR_WORKSPACE: return "workspace missing or too small";
     case MLA_ERR_HIP: return "HIP runtime or launch failure";
     case MLA_ERR_UNSUPPORTED: return "device is not gfx950";
+    case MLA_ERR_SCRATCH: return "call needs more than the fixed device scratch of the allocation-free entry point";
     default: return "unknown error code";
   }
 }

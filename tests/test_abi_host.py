@@ -291,3 +291,23 @@ def test_gather_probe_invalid_arguments(lib):
         rc = lib.mla_probe_gather_rows(a["c"], a["r"], a["rows"], a["stride"], a["idx"], a["g"], a["k"],
                                        a["t"], a["s"], None)
         assert rc == B.MLA_ERR_INVALID, bad
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """A call whose partials exceed the fixed 64 MiB device scratch is refused
+    with MLA_ERR_SCRATCH before any HIP call (300 sequences x 2 row blocks x
+    4 records of 33,152 bytes = 79.6 MB); its workspace twin would accept it
+    with a large enough workspace."""
+    d = _dims(batch=300, num_q=4, num_heads=64, max_kv_len=5000, kv_rows=300 * 5000,
+              kv_seq_stride=5000)
+    need = mv.workspace_bytes(d)
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    p = P()
+    rc = lib.mla_verify_attn_noalloc(ctypes.byref(d), p, p, p, p, None, None, p,
+                                     ctypes.c_float(0.1), p, p, None)
+    assert rc == B.MLA_ERR_SCRATCH
+    assert "scratch" in mv.strerror(B.MLA_ERR_SCRATCH)
+    # invalid arguments are still MLA_ERR_INVALID first
+    rc = lib.mla_verify_attn_noalloc(ctypes.byref(d), None, p, p, p, None, None, p,
+                                     ctypes.c_float(0.1), p, p, None)
+    assert rc == B.MLA_ERR_INVALID
