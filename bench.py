@@ -138,6 +138,8 @@ def _cpu_model():
     import subprocess
 
     try:
+        if _profiled():
+            raise RuntimeError("no child programs under the profiler")
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
         for line in out.splitlines():
             if line.startswith("Model name:"):
@@ -265,7 +267,20 @@ def main():
     copies = vc.copies
     smi_before = smi_snapshot()
 
+    # ---- ceilings first: the matrix-core probe runs for at least SETTLE_S seconds,
+    # which also takes the GPU out of its idle clock state, so the timed calls run
+    # at the clock a busy GPU holds (from idle, the first few ms of calls run at
+    # ~1.5 GHz instead of ~1.85: 20 calls after 5 warm-up calls measured 161.5
+    # instead of 151.3 us on workload 3) -----------------------------------------
+    gather = vc.gather_probe() if w.layout == "sparse" else None
+    ceil = measured_ceilings(dev, gather, settle_s=SETTLE_S)
+    # host-side gaps of a few ms (allocations, syncs, Python) let the clock fall
+    # again, so every timed loop below is enqueued right behind ~15 ms of probe
+    # work with no host wait in between
+    busy = KeepBusy(dev, stream)
+
     # ---- warmup -----------------------------------------------------------------------
+    busy()
     for i in range(args.warmup):
         call(copies[i % len(copies)])
     torch.cuda.synchronize()
@@ -291,6 +306,7 @@ def main():
 
     # ---- per-call spread (events around each call, outside the timed region) -----------
     evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    busy()
     for i in range(K):
         evc[i][0].record(stream)
         call(copies[i % len(copies)])
@@ -301,6 +317,7 @@ def main():
     log(f"per-call us: {pct}")
 
     # ---- warm (one copy, Infinity-Cache resident) for context ----------------------------
+    busy()
     t_start.record(stream)
     for i in range(K):
         call(copies[0])
@@ -319,6 +336,7 @@ def main():
             call(c, st=side)
     torch.cuda.synchronize()
     reps = max(1, K // len(copies))
+    busy()
     t_start.record(stream)
     for _ in range(reps):
         graph.replay()
@@ -329,12 +347,13 @@ def main():
     del graph
 
     # ---- four calls in flight on four streams (own outputs and workspaces) -----------------
-    streams4_us = vc.streams_throughput(4, K)
+    streams4_us = vc.streams_throughput(4, K, busy)
     log(f"4 streams: {streams4_us:.2f} us per call ({K} calls dealt over 4 streams)")
 
     # ---- per-kernel durations: back-to-back launches of each phase between two events -------
     # on the launch stream (the rotated copies as in the timed region); each average
     # is one launch's duration plus the gap to the next launch on the same queue
+    busy()
     t_start.record(stream)
     for i in range(K):
         call(copies[i % len(copies)], mv.binding.PHASE_PARTIAL)
@@ -343,6 +362,7 @@ def main():
     split_ms = t_start.elapsed_time(t_end) / K
     combine_ms = 0.0
     if vc.info.workspace_bytes > 0:
+        busy()
         t_start.record(stream)
         for i in range(K):
             call(copies[i % len(copies)], mv.binding.PHASE_COMBINE)
@@ -367,11 +387,10 @@ def main():
                     unit="GB/s", frac=round(achieved / PEAK_HBM_GBPS, 4))
     roof["traffic"] = None if spiked else load_traffic(w.spec.name)
     roof["kernel"] = "mla_split_kernel"
-    # The same kernel against what this GPU measurably sustains: a full-load bf16
-    # MFMA loop (matrix-core bound), or for HBM-bound calls the same rows gathered
-    # with no compute (sparse) or else a 256 MiB device copy.
-    gather = vc.gather_probe() if w.layout == "sparse" else None
-    ceil = measured_ceilings(dev, gather)
+    # The same kernel against what this GPU measurably sustains (measured before
+    # the timed calls): a full-load bf16 MFMA loop (matrix-core bound), or for
+    # HBM-bound calls the same rows gathered with no compute (sparse) or else a
+    # 256 MiB device copy.
     if roof["bound"] == "mfma":
         measured = ceil["mfma_bf16_TFLOPs"]
     else:
@@ -421,7 +440,7 @@ def main():
         "algorithmic_flops": wm["flops"],
         "roofline": roof,
         "measured_ceilings": ceil,
-        "clocks": {"shader_GHz_after_timed_calls": clock_after,
+        "clocks": {"settle_s": SETTLE_S, "shader_GHz_after_timed_calls": clock_after,
                    "shader_GHz_full_mfma_load": ceil.get("probe_clock_GHz"),
                    "smi_before": smi_before, "smi_after": smi_after},
         "cpu_baseline": cpu,
@@ -432,6 +451,7 @@ def main():
 
 
 MALL_BYTES = 256 * 2**20  # MI355X Infinity Cache
+SETTLE_S = 0.25  # seconds of matrix-core probe before any timed call
 MAX_COPIES = 128
 
 
@@ -521,7 +541,7 @@ class VerifyCall:
                            self.kv_lens, w.scale, out, lse, workspace=ws, stream=st, phase=phase,
                            **self.kw)
 
-    def streams_throughput(self, n, calls):
+    def streams_throughput(self, n, calls, busy=None):
         """µs per call with `calls` whole calls dealt round-robin over n streams
         (each stream its own outputs and workspace, inputs cycling over the
         copies), from one event on the launch stream before the first and one
@@ -537,6 +557,8 @@ class VerifyCall:
                       ws=wss[k])
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if busy is not None:
+            busy()
         e0.record(self.stream)
         for s in streams:
             s.wait_stream(self.stream)
@@ -569,6 +591,24 @@ class VerifyCall:
         return gather
 
 
+class KeepBusy:
+    """Enqueues `launches` matrix-core probe launches (~0.6 ms each on one
+    workgroup per CU) with no host wait, so work enqueued next starts on a GPU
+    that has not idled."""
+
+    def __init__(self, dev, stream, launches=24, iters=2000):
+        import torch
+
+        self.blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+        self.sink = torch.empty(self.blocks * 256, dtype=torch.float32, device=dev)
+        self.stream, self.launches, self.iters = stream, launches, iters
+
+    def __call__(self):
+        import speculative_decode_verify_mla_amd as mv
+        for _ in range(self.launches):
+            mv.probe_mfma_bf16(self.blocks, self.iters, self.sink, stream=self.stream)
+
+
 class ClockProbe:
     """A short launch of the matrix-core probe (one workgroup per CU) whose
     in-kernel stamps give the shader clock: s_memtime cycles over 100 MHz
@@ -590,10 +630,20 @@ class ClockProbe:
         return round(s[0] / s[1] * 0.1, 3) if s[1] > 0 else None
 
 
+def _profiled():
+    """True under rocprofv3: its preloaded library initialises the GPU in every
+    child process too, so no child program may be started then."""
+    pre = os.environ.get("LD_PRELOAD", "")
+    return "rocprof" in pre or any(k.startswith("ROCPROF") for k in os.environ)
+
+
 def smi_snapshot():
-    """Clocks, power and driver as rocm-smi reports them (JSON), or None."""
+    """Clocks, power and driver as rocm-smi reports them (JSON), or None
+    (also when profiled: see _profiled)."""
     import subprocess
 
+    if _profiled():
+        return None
     try:
         res = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showdriverversion",
                               "--showproductname", "--json"],
@@ -622,6 +672,8 @@ def bench_sweep(args, dev):
     from speculative_decode_verify_mla_amd import synth
 
     lds = 160 * 1024
+    measured_ceilings(dev, None, settle_s=SETTLE_S)  # out of the idle clock state first
+    busy = KeepBusy(dev, torch.cuda.current_stream(dev))
     rows = []
     for T in (16, 1):
         for L in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
@@ -630,6 +682,7 @@ def bench_sweep(args, dev):
             wm = work_model(w)
             ncopies = auto_copies(wm["total_bytes"], 2)
             vc = VerifyCall(w, dev, ncopies, 0)
+            busy()
             for i in range(args.warmup):
                 vc.call(vc.copies[i % ncopies])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -669,13 +722,14 @@ def device_info(dev):
             "hbm_GiB": round(p.total_memory / 2**30, 1), "hip": torch.version.hip}
 
 
-def measured_ceilings(dev, gather=None):
+def measured_ceilings(dev, gather=None, settle_s=0.0):
     """Best-of-5 rates of (a) the library's matrix-core probe, 16 independent
     bf16 32x32x16 MFMA chains per wave on every CU (with the shader clock its
     in-kernel stamps read), (b) a 256 MiB device-to-device copy (read + write
     bytes) and, when `gather` is given (a call that enqueues the library's
     row-gather probe, and returns its bytes when called with count=True), (c)
-    that gather. All are event-timed on the current stream."""
+    that gather. All are event-timed on the current stream. With settle_s, the
+    matrix-core probe first runs back to back for that many seconds."""
     import torch
 
     import speculative_decode_verify_mla_amd as mv
@@ -708,6 +762,12 @@ def measured_ceilings(dev, gather=None):
         if s[1] > 0:
             clocks.append(s[0] / s[1] * 0.1)
 
+    if settle_s > 0:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(8):
+                mv.probe_mfma_bf16(blocks, iters, sink, stream=stream)
+            torch.cuda.synchronize()
     t_mfma = best(lambda: mv.probe_mfma_bf16(blocks, iters, sink, stream=stream), after=read_clock)
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)

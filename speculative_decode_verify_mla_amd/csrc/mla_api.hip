@@ -120,9 +120,16 @@ int make_plan(const mla_dims* d, bool sparse, mla_plan_info* p) {
     // kernels share them out by the sequences' actual lengths (kv_lens lives on
     // the device) and spread each sequence's tiles evenly over its slots.
     if (groups == 1) {
-      // One sequence: every slot is one of its splits.
-      slots = d->num_splits > 0 ? std::min<int64_t>(std::min<int64_t>(d->num_splits, tiles), mlav::kMaxSplits)
-                                : std::max<int64_t>(1, std::min<int64_t>(kPlanCUs / row_blocks, cap));
+      // One sequence: every slot is one of its splits. Automatic: the fewest
+      // splits whose longest one is as short as one workgroup per CU allows
+      // (65 tiles over at most 32 slots: 22 splits of at most 3 tiles, not 32
+      // of 2-3, which only add partials to write and combine).
+      if (d->num_splits > 0) {
+        slots = std::min<int64_t>(std::min<int64_t>(d->num_splits, tiles), mlav::kMaxSplits);
+      } else {
+        const int64_t most = std::max<int64_t>(1, std::min<int64_t>(kPlanCUs / row_blocks, cap));
+        slots = ceil_div(tiles, ceil_div(tiles, most));
+      }
       splits = slots;
     } else if (d->num_splits > 0) {
       // A requested split count fixes the chunk every sequence is cut by.

@@ -155,13 +155,18 @@ def test_plan_shapes():
     assert p8.num_splits == 3  # 132 keys = 3 tiles
 
 
-def test_plan_single_sequence_fills_every_slot():
-    # Kimi-like verify (65 tiles, 8 row blocks): 32 splits of 2-3 tiles each, so
-    # 256 workgroups, not 22 splits of 3 (176 workgroups)
+def test_plan_single_sequence_fewest_splits_of_the_shortest_chunk():
+    # Kimi-like verify (65 tiles, 8 row blocks, at most 32 slots): no split can
+    # hold fewer than 3 tiles at most, and 22 splits of at most 3 reach that
+    # (32 splits of 2-3 would only add partials to write and combine)
     d = _dims(num_q=16, num_heads=64, max_kv_len=4112, kv_rows=4112, kv_seq_stride=4112)
     p = mv.plan(d)
-    assert (p.row_blocks, p.split_slots, p.num_splits, p.chunk_tiles) == (8, 32, 32, 3)
-    assert p.workspace_bytes == 32 * 8 * 4 * (32 * 512 * 2 + 3 * 32 * 4)
+    assert (p.row_blocks, p.split_slots, p.num_splits, p.chunk_tiles) == (8, 22, 22, 3)
+    assert p.workspace_bytes == 22 * 8 * 4 * (32 * 512 * 2 + 3 * 32 * 4)
+    # a requested count is taken as it is (capped at the tiles)
+    p2 = mv.plan(_dims(num_q=16, num_heads=64, max_kv_len=4112, kv_rows=4112,
+                       kv_seq_stride=4112, num_splits=32))
+    assert (p2.num_splits, p2.chunk_tiles) == (32, 3)
 
 
 def _plan_tuple(d, sparse=False):
