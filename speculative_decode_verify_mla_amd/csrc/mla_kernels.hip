@@ -911,11 +911,17 @@ static_assert(16 * 256 * 4 == kRecElems, "16 combine blocks of 256 threads x 4 d
 // The combine of one block once its split count is known; KBATCH (8, 16, 32) is
 // the number of splits whose loads are issued together, chosen from the count
 // so that a block with few splits issues no loads it does not use.
+// With `part` (the first stage of a two-stage combine, for groups of more than
+// 32 splits): the block merges only its chunk of splits and writes, instead of
+// out/lse, the chunk's unnormalised fp32 sum (part, register-native order) and
+// per row its log2 maxima and sums (part_st: max of the rounded-term log2
+// sums, their weight sum, max of the fp32-term ones, their sum).
 template <int KBATCH>
 __device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMaxSplits + 1],
                                              float (*red)[8][kRowsPerWave], float* row_lse,
                                              float* row_inv, int rb, int group, int wave, int db,
-                                             int n_active, int64_t rec0, int64_t rec_stride) {
+                                             int n_active, int64_t rec0, int64_t rec_stride,
+                                             float* part = nullptr, float* part_st = nullptr) {
   constexpr int kBatch = KBATCH;
   const int t = threadIdx.x;
   const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
@@ -1004,6 +1010,12 @@ __device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMa
     if (sl == 0) row_inv[r] = ws > 0.f ? 1.0f / ws : 0.f;
     if (sl == 0)
       row_lse[r] = (mx != -__builtin_inff() && es > 0.f) ? (mx + fast_log2(es)) * kLn2 : -__builtin_inff();
+    if (part_st != nullptr && sl == 0 && db == 0) {
+      part_st[r] = mxq;
+      part_st[kRowsPerWave + r] = ws;
+      part_st[2 * kRowsPerWave + r] = mx;
+      part_st[3 * kRowsPerWave + r] = es;
+    }
     __syncthreads();
   }
 
@@ -1027,6 +1039,10 @@ __device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMa
       }
     }
   }
+  if (part != nullptr) {
+    *reinterpret_cast<f32x4*>(part + ((db * 4 + qq) * 64 + lane) * 4) = acc;
+    return;
+  }
   if (row >= a.rows_per_group) return;
   const float inv = row_inv[l32];
   acc[0] *= inv;
@@ -1040,6 +1056,137 @@ __device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMa
   pkd.y = pack_bf16x2(acc[2], acc[3]);
   *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
   if (db == 0 && qq == 0 && half == 0) a.lse[qrow] = row_lse[l32];
+}
+
+// The splits holding keys of a group, and where its records of one (row block,
+// wave) start and step (shared by the combine kernels).
+template <bool kSparseMode>
+__device__ __forceinline__ void group_records(const MainArgs& a, int group, int rb, int wave,
+                                              int& n_active, int64_t& rec0, int64_t& rec_stride) {
+  const GroupInfo gi = group_info(a, group, kSparseMode);
+  if (kSparseMode) {
+    n_active = min(a.num_splits, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
+    rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
+    rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
+  } else {
+    int slot0;
+    if (a.num_groups == 1) {
+      slot0 = 0;
+      n_active = dense_active(gi.n_tiles, a.split_slots);
+    } else {
+      const int2 m = a.ws_meta[group];  // written by the split kernel
+      slot0 = m.x;
+      n_active = m.y;
+    }
+    rec0 = ((int64_t)slot0 * a.row_blocks + rb) * kWaves + wave;
+    rec_stride = (int64_t)a.row_blocks * kWaves;
+  }
+}
+
+// Two-stage combine, first stage: block = (wave record, chunk c of 32 splits,
+// 32-dim block) merges splits 32c .. 32c+31 into the chunk record
+// (record * part_chunks + c) of ws_part. A chunk past the group's splits
+// writes zero weights, so the second stage skips it.
+template <int MODE>
+__global__ void __launch_bounds__(256) mla_combine_part_kernel(MainArgs a) {
+  constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
+  __shared__ float wts[kRowsPerWave][kMaxSplits + 1];
+  __shared__ float red[3][8][kRowsPerWave];
+  __shared__ float row_lse[kRowsPerWave];
+  __shared__ float row_inv[kRowsPerWave];
+
+  const int bid = blockIdx.x;
+  const int db = bid & 15;
+  const int rest = bid >> 4;
+  const int c = rest % a.part_chunks;
+  const int wrec = rest / a.part_chunks;
+  const int wave = wrec & 3;
+  const int rbg = wrec >> 2;
+  const int rb = rbg % a.row_blocks;
+  const int group = rbg / a.row_blocks;
+  if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;  // padding wave record
+  int n_active;
+  int64_t rec0, rec_stride;
+  group_records<kSparseMode>(a, group, rb, wave, n_active, rec0, rec_stride);
+  if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
+  const int64_t prec = (int64_t)wrec * a.part_chunks + c;
+  float* part = a.ws_part + prec * kRecElems;
+  float* part_st = a.ws_part + (int64_t)a.num_groups * a.row_blocks * kWaves * a.part_chunks * kRecElems +
+                   prec * (4 * kRowsPerWave);
+  const int n_c = min(32, n_active - 32 * c);
+  if (n_c <= 0) {
+    if (db == 0 && threadIdx.x < kRowsPerWave) {
+      part_st[threadIdx.x] = -__builtin_inff();
+      part_st[kRowsPerWave + threadIdx.x] = 0.f;
+      part_st[2 * kRowsPerWave + threadIdx.x] = -__builtin_inff();
+      part_st[3 * kRowsPerWave + threadIdx.x] = 0.f;
+    }
+    return;
+  }
+  const int64_t r0 = rec0 + (int64_t)(32 * c) * rec_stride;
+  if (n_c <= 8)
+    combine_rows<8>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c, r0, rec_stride, part, part_st);
+  else if (n_c <= 16)
+    combine_rows<16>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c, r0, rec_stride, part, part_st);
+  else
+    combine_rows<32>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c, r0, rec_stride, part, part_st);
+}
+
+// Second stage: block = (wave record, 32-dim block); each thread merges the
+// chunks' sums of 4 dims of one row: out = sum_c 2^(mq_c - M) A_c / sum_c
+// 2^(mq_c - M) W_c, lse = log2 sum_c 2^(me_c) E_c (natural log on output).
+template <int MODE>
+__global__ void __launch_bounds__(256) mla_combine_chunks_kernel(MainArgs a) {
+  constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
+  const int bid = blockIdx.x;
+  const int db = bid & 15;
+  const int wrec = bid >> 4;
+  const int wave = wrec & 3;
+  const int rbg = wrec >> 2;
+  const int rb = rbg % a.row_blocks;
+  const int group = rbg / a.row_blocks;
+  if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;
+  int n_active;
+  int64_t rec0, rec_stride;
+  group_records<kSparseMode>(a, group, rb, wave, n_active, rec0, rec_stride);
+  if (n_active <= 1) return;
+  const int n_chunks = min(a.part_chunks, (n_active + 31) / 32);
+  const int t = threadIdx.x;
+  const int lane = t & 63, qq = t >> 6, half = lane >> 5, l32 = lane & 31;
+  const int64_t prec0 = (int64_t)wrec * a.part_chunks;
+  const float* st0 = a.ws_part + (int64_t)a.num_groups * a.row_blocks * kWaves * a.part_chunks * kRecElems +
+                     prec0 * (4 * kRowsPerWave) + l32;
+  float mq = -__builtin_inff(), me = -__builtin_inff();
+  for (int c = 0; c < n_chunks; ++c) {
+    mq = fmaxf(mq, st0[c * 4 * kRowsPerWave]);
+    me = fmaxf(me, st0[c * 4 * kRowsPerWave + 2 * kRowsPerWave]);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f, esum = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    const float* st = st0 + c * 4 * kRowsPerWave;
+    const float wq = st[kRowsPerWave];
+    const float e = st[3 * kRowsPerWave];
+    if (e > 0.f) esum += fast_exp2(st[2 * kRowsPerWave] - me) * e;
+    if (wq > 0.f) {
+      const float f = fast_exp2(st[0] - mq);
+      wsum += f * wq;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_part + (prec0 + c) * kRecElems +
+                                                        ((db * 4 + qq) * 64 + lane) * 4);
+      acc += f * v;
+    }
+  }
+  const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
+  if (row >= a.rows_per_group) return;
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  const int64_t qrow = (int64_t)group * a.rows_per_group + row;
+  const int d = db * 32 + 8 * qq + 4 * half;
+  uint2 pkd;
+  pkd.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pkd.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
+  if (db == 0 && qq == 0 && half == 0)
+    a.lse[qrow] = (me != -__builtin_inff() && esum > 0.f) ? (me + fast_log2(esum)) * kLn2 : -__builtin_inff();
 }
 
 template <int MODE>
@@ -1103,6 +1250,14 @@ static hipError_t launch_split(const MainArgs& a, hipStream_t s) {
 template <int MODE>
 static hipError_t launch_combine(const MainArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)a.num_groups * (unsigned)a.row_blocks * kWaves * 16u;
+  if (a.part_chunks > 0) {
+    hipLaunchKernelGGL(mla_combine_part_kernel<MODE>, dim3(grid * (unsigned)a.part_chunks), dim3(256),
+                       0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_combine_chunks_kernel<MODE>, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(mla_combine_kernel<MODE>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -418,3 +418,38 @@ def test_reference_rises_several_times_in_a_split(gpu_lib):
     for s in (1, 0, 3):
         d.run(num_splits=s)
         _check(*d.results(), ref_out, ref_lse, tag=f"three rises splits={s}")
+
+
+@pytest.mark.parametrize("layout", ["contig", "sparse"])
+def test_two_stage_combine_many_splits(gpu_lib, layout):
+    """Groups of more than 32 splits (one sequence, or sparse tokens) merge in
+    two stages: chunks of 32 splits, then the chunks. Split counts of 33..79,
+    a last chunk of a single split, and a sequence shorter than the planned
+    length (its last planned chunks hold no split) all match the oracle."""
+    import dataclasses
+    if layout == "contig":
+        spec = Spec("many_splits", B=1, T=2, H=64, layout="contig", prefix=5000)
+        w = generate(spec, seed=28)
+        _announce("two-stage combine, one sequence", w)
+        d = _dev(w)
+        ref = run_oracle(w)
+        for splits in (33, 60, 65, 79):
+            d.run(num_splits=splits)
+            _check(*d.results(), *ref, tag=f"many splits s={splits}")
+        # the same cache and plan, but the sequence is only 3000 keys long
+        w2 = dataclasses.replace(w, kv_lens=np.array([3000], np.int32))
+        d2 = _dev(w2)
+        d2.w = dataclasses.replace(w2, max_kv_len=w.max_kv_len)
+        ref2 = run_oracle(w2)
+        d2.run(num_splits=79)
+        _check(*d2.results(), *ref2, tag="many splits, shorter sequence")
+    else:
+        spec = Spec("many_splits_sparse", B=2, T=2, H=64, layout="sparse", cache_len=9000,
+                    topk=3000)
+        w = generate(spec, seed=29)
+        _announce("two-stage combine, sparse", w)
+        d = _dev(w)
+        ref = run_oracle(w)
+        for splits in (33, 47):
+            d.run(num_splits=splits)
+            _check(*d.results(), *ref, tag=f"sparse many splits s={splits}")
