@@ -27,10 +27,11 @@
 //    permuted identically on both operands). V^T comes from the row-major tile
 //    through ds_read_b64_tr_b16 (transposing LDS read), so K and V share one
 //    tile (MLA's value rows are the first 512 dims of its key rows).
-//  * The 256 accumulator registers per lane are never rescaled in the loop (a
-//    VALU rescale would pull them out of the accumulation registers): exponents
-//    use a fixed per-row reference, with an exact two-pass fallback when a
-//    later score exceeds it by more than 2^32.
+//  * The 256 accumulator registers per lane are not rescaled tile by tile (a
+//    VALU rescale in the loop pulls them out of the accumulation registers):
+//    exponents use a fixed per-row reference, raised by an exact power of two
+//    at the end of a tile whose terms sum past 2^32, with a two-pass fallback
+//    when a single tile exceeds it by more than 2^96.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,6 +46,10 @@ constexpr int kRopeBytes = kTile * kDR * 2;   // 8192: rope part of a tile
 constexpr int kStageBytes = kLatBytes + kRopeBytes;  // 73728
 constexpr int kStages = 2;
 constexpr int kLdsBytes = kStages * kStageBytes;  // 147456
+constexpr int kQLatBytes = kRowsPerWave * kDL * 2;           // 32768: a wave's latent query rows
+constexpr int kQWaveBytes = kQLatBytes + kRowsPerWave * kDR * 2;  // 36864: with the rope rows
+static_assert(kWaves * kQWaveBytes == kLdsBytes && 2 * kQWaveBytes == kStageBytes,
+              "a row block's query rows fill both stages, two waves' rows one stage");
 static_assert(kLdsBytes + 16 <= 163840, "two KV stages must fit one gfx950 CU's 160 KB LDS");
 constexpr int kLoadsPerStage = kStageBytes / (64 * 16);  // 72 wave-wide 16-byte loads
 static_assert(kLoadsPerStage == 72 && kLoadsPerStage % kWaves == 0, "load split");
@@ -469,9 +474,9 @@ mla_split_kernel(MainArgs a) {
   constexpr int kLoadsPerWave = 18;
 
   // The first tile of the split (re-issued by a second pass). Dense: issued
-  // before the query loads so that its HBM latency overlaps theirs. (Sparse
-  // issues it in the pass loop: holding its index state across the query loads
-  // costs the gather loop spilled registers.)
+  // with the query rows' DMA when they fit in stage 1, else right after the
+  // rows are read out of LDS. (Sparse issues it in the pass loop: holding its
+  // index state across the query rows costs the gather loop spilled registers.)
   int nv_cur = 0, nv_next = 0;
   uint64_t vm_cur = 0, vm_next = 0;
   int idx_next = -1;
@@ -490,22 +495,61 @@ mla_split_kernel(MainArgs a) {
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) load_one(tl0, i);
   };
-  if (!kSparseMode) issue_first_tile();
-
-  // ---- query rows into registers: the B operand of S^T = K Q^T ------------
-  // Lane (row l32, half h) holds dims 16c + 8h .. +7 of chunk c (c < 32: latent).
-  // Padding rows (past the group's rows) compute a copy of the group's row 0;
-  // they are never written out.
-  bf16x8 q[36];
-  {
-    const int64_t qsrc = row_valid ? qrow : (int64_t)group * a.rows_per_group;
+  // ---- query rows: HBM -> LDS by DMA, then into registers ------------------
+  // Register q[c] of lane (row l32, half h) holds 16-byte chunk 2c + h of the
+  // row's 1,152 bytes (chunks 0..63: latent, 64..71: rope): the B operand of
+  // S^T = K Q^T. Loaded straight into that layout, every load instruction
+  // touches 32 rows, 32 bytes each, and the wave's 36 loads take twice as long
+  // to go through the memory path as the same bytes read a whole 1 KiB row per
+  // instruction. So each wave DMAs its 32 rows into LDS, one row (or 8 rope
+  // rows) per instruction, and reads its fragments from there. In LDS a latent
+  // row r holds chunk k at slot k ^ (r & 15), a rope row r at slot
+  // k ^ ((r >> 1) & 7), which makes the 16-byte reads of 16 rows' same chunk
+  // conflict-free. Rows past the group's end read as zero (they are never
+  // written out). A row block of at most 64 rows (two waves) stages its rows in
+  // stage 1 while the first tile streams into stage 0; a larger one needs both
+  // stages, so its first tile waits until every wave holds its rows.
+  const bool q_in_stage1 = a.rows_per_group - rb * kRowsPerBlock <= 2 * kRowsPerWave;
+  uint8_t* const q_lds = smem + (q_in_stage1 ? kStageBytes : 0) + wave * kQWaveBytes;
+  if (!kSparseMode && q_in_stage1) issue_first_tile();
+  if (wave_active) {
+    const int nrows = min(kRowsPerWave, a.rows_per_group - row0);
+    const int64_t qbase = (int64_t)group * a.rows_per_group + row0;
+    const auto ql = make_rsrc(a.q_lat + qbase * kDL, (uint32_t)nrows * 1024u);
+    const auto qr = make_rsrc(a.q_rope + qbase * kDR, (uint32_t)nrows * 128u);
 #pragma unroll
-    for (int c = 0; c < 36; ++c) {
-      const uint16_t* src = c < 32 ? a.q_lat + qsrc * kDL + 16 * c + 8 * half
-                                   : a.q_rope + qsrc * kDR + 16 * (c - 32) + 8 * half;
-      q[c] = *reinterpret_cast<const bf16x8*>(src);
+    for (int c = 0; c < kRowsPerWave; ++c)
+      buffer_to_lds(ql, q_lds + c * 1024, (unsigned)(c * 1024 + 16 * (lane ^ (c & 15))));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 8 * j + (lane >> 3);
+      buffer_to_lds(qr, q_lds + kQLatBytes + j * 1024,
+                    (unsigned)(r * 128 + 16 * ((lane & 7) ^ ((r >> 1) & 7))));
     }
   }
+  bf16x8 q[36];
+  auto read_query = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);  // the rows' DMA landed
+    if (wave_active) {
+      // chunk 2c + h of latent row r sits at r*1024 + 16*((2c + h) ^ (r & 15)) =
+      // (lb ^ 32*(c % 8)) + 256*(c / 8), lb = r*1024 + 16*(h ^ (r & 15)); rope
+      // chunk 2j + h at rb ^ 32j, rb = 32768 + r*128 + 16*(h ^ ((r >> 1) & 7)).
+      // The bases are opaque here, so the compiler builds the 36 offsets at the
+      // reads instead of hoisting them to the prologue (and spilling them).
+      unsigned lb = (unsigned)(l32 * 1024 + 16 * (half ^ (l32 & 15)));
+      unsigned rbq = (unsigned)(kQLatBytes + l32 * 128 + 16 * (half ^ ((l32 >> 1) & 7)));
+      asm volatile("" : "+v"(lb), "+v"(rbq));
+#pragma unroll
+      for (int c = 0; c < 36; ++c) {
+        const unsigned off = c < 32 ? (lb ^ (unsigned)(32 * (c & 7))) + (unsigned)(256 * (c >> 3))
+                                    : rbq ^ (unsigned)(32 * (c - 32));
+        q[c] = lds_read16(q_lds, off);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 36; ++c) q[c] = bf16x8{};
+    }
+  };
 
   // ---- visibility of the T draft keys for this lane's row (dense) ----------
   uint64_t vis = 0;
@@ -544,6 +588,18 @@ mla_split_kernel(MainArgs a) {
     }
   }
 
+
+  // Sparse calls with the rows in stage 1 read them once the first gather is
+  // out (in the pass loop); the others now.
+  const bool q_after_gather = kSparseMode && q_in_stage1;
+  if (!q_after_gather) {
+    read_query();
+    if (!q_in_stage1) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's reads of both stages are done
+      __syncthreads();                // ... and every other wave's
+      if (!kSparseMode) issue_first_tile();
+    }
+  }
 
   // ---- softmax state ------------------------------------------------------------
   // Exponents are taken against a per-row reference m_ref (log2 units), not a
@@ -667,6 +723,7 @@ mla_split_kernel(MainArgs a) {
     bool overflow = false;
 
     if (kSparseMode || pass > 0) issue_first_tile();  // stage 0 is free: a pass ends on a barrier
+    if (q_after_gather && pass == 0) read_query();
     if (threadIdx.x == 0) *restart_flag = 0;
 
     for (int tile = t_begin; tile < t_end; ++tile) {
