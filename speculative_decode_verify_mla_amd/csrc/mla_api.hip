@@ -94,11 +94,11 @@ int check_device() {
   return st == 1 ? MLA_OK : MLA_ERR_UNSUPPORTED;
 }
 
-// Chunks of 32 splits for a two-stage combine: groups of more than 32 splits
+// Chunks of 16 splits for a two-stage combine: groups of more than 32 splits
 // whose split count the host knows (sparse calls: uniform; one dense sequence:
 // its slots); 0 = one-stage combine.
 int64_t plan_part_chunks(bool sparse, int64_t groups, int64_t splits) {
-  if (!(sparse || groups == 1) || splits <= mlav::kPartSplits) return 0;
+  if (!(sparse || groups == 1) || splits <= mlav::kPartOneStageMax) return 0;
   return ceil_div(splits, mlav::kPartSplits);
 }
 

@@ -29,9 +29,11 @@ constexpr int kMinChunkDense = 2;
 constexpr int kMinChunkSparse = 4;
 constexpr size_t kRecBytes = (size_t)kRecElems * 2 + (size_t)kRecRowStats * kRowsPerWave * 4;
 // Two-stage combine (groups of more than 32 splits, when a group's split count
-// is known on the host): one chunk record per (wave record, 32 splits), an fp32
+// is known on the host): one chunk record per (wave record, 16 splits), an fp32
 // sum of 32 rows x 512 dims plus 4 floats per row.
-constexpr int kPartSplits = 32;
+constexpr int kPartSplits = 16;
+constexpr int kPartOneStageMax = 32;  // up to this many splits a group combines in one stage
+constexpr int kMaxPartChunks = kMaxSplits / kPartSplits;
 constexpr size_t kPartRecBytes = (size_t)kRecElems * 4 + (size_t)4 * kRowsPerWave * 4;
 
 enum Mode : int { kContig = 0, kPaged = 1, kSparse = 2, kSparsePaged = 3 };
@@ -68,7 +70,7 @@ struct MainArgs {
   int32_t slot_stride;  // dense: workgroups per row block in the grid (= split_slots)
   int32_t fixed_chunk;  // dense: tiles per split when requested, 0 = chosen on the device
   int32_t final_out;    // 1: single split for every group, write out/lse directly
-  int32_t part_chunks;  // > 0: combine in two stages over chunks of 32 splits (groups of > 32 splits)
+  int32_t part_chunks;  // > 0: combine in two stages over chunks of 16 splits (groups of > 32 splits)
   float scale_log2;    // scale * log2(e)
 };
 

@@ -965,20 +965,25 @@ mla_split_kernel(MainArgs a) {
 // ---------------------------------------------------------------------------
 static_assert(16 * 256 * 4 == kRecElems, "16 combine blocks of 256 threads x 4 dims cover one wave record");
 
-// The combine of one block once its split count is known; KBATCH (8, 16, 32) is
-// the number of splits whose loads are issued together, chosen from the count
-// so that a block with few splits issues no loads it does not use.
+// The combine of one block; KBATCH (8, 16, 32) is the number of splits whose
+// loads are issued together, chosen from the planned count n_plan so that a
+// block with few splits issues no loads it does not use. The loads are clamped
+// to the planned splits (whose records exist) and issued before the actual
+// count n_active <= n_plan, which depends on kv_lens, is used: the kv_lens
+// round trip overlaps the workspace loads. A block whose group ended up with
+// one split (written out by the split kernel itself) returns after the loads.
 // With `part` (the first stage of a two-stage combine, for groups of more than
 // 32 splits): the block merges only its chunk of splits and writes, instead of
 // out/lse, the chunk's unnormalised fp32 sum (part, register-native order) and
 // per row its log2 maxima and sums (part_st: max of the rounded-term log2
 // sums, their weight sum, max of the fp32-term ones, their sum).
 template <int KBATCH>
-__device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMaxSplits + 1],
+__device__ __forceinline__ bool combine_rows(const MainArgs& a, float (*wts)[kMaxSplits + 1],
                                              float (*red)[8][kRowsPerWave], float* row_lse,
                                              float* row_inv, int rb, int group, int wave, int db,
-                                             int n_active, int64_t rec0, int64_t rec_stride,
-                                             float* part = nullptr, float* part_st = nullptr) {
+                                             int n_plan, int n_active, int64_t rec0, int64_t rec_stride,
+                                             float* part = nullptr, float* part_st = nullptr,
+                                             bool go = true) {
   constexpr int kBatch = KBATCH;
   const int t = threadIdx.x;
   const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
@@ -1000,7 +1005,7 @@ __device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMa
 #pragma unroll
   for (int i = 0; i < kHeld; ++i) {
     const int s = sl + 8 * i;
-    const int sc = min(s, n_active - 1);
+    const int sc = min(s, n_plan - 1);
     const float le = st[sc * st_step], lq = st[sc * st_step + kRowsPerWave];
     const float sf = st[sc * st_step + 2 * kRowsPerWave];
     const bool v = s < n_active;
@@ -1013,7 +1018,8 @@ __device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMa
   uint2 raw[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    raw[j] = *reinterpret_cast<const uint2*>(o_p + min(j, n_active - 1) * o_step);
+    raw[j] = *reinterpret_cast<const uint2*>(o_p + min(j, n_plan - 1) * o_step);
+  if (!go || n_active < 1) return false;  // (block-uniform)
 
   // ---- phase 1: per-row maxima, sums and weights (thread = row x split lane) ----
   {
@@ -1098,9 +1104,9 @@ __device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMa
   }
   if (part != nullptr) {
     *reinterpret_cast<f32x4*>(part + ((db * 4 + qq) * 64 + lane) * 4) = acc;
-    return;
+    return true;
   }
-  if (row >= a.rows_per_group) return;
+  if (row >= a.rows_per_group) return true;
   const float inv = row_inv[l32];
   acc[0] *= inv;
   acc[1] *= inv;
@@ -1113,37 +1119,43 @@ __device__ __forceinline__ void combine_rows(const MainArgs& a, float (*wts)[kMa
   pkd.y = pack_bf16x2(acc[2], acc[3]);
   *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
   if (db == 0 && qq == 0 && half == 0) a.lse[qrow] = row_lse[l32];
+  return true;
 }
 
-// The splits holding keys of a group, and where its records of one (row block,
-// wave) start and step (shared by the combine kernels).
+// The splits planned for a group (their records exist) and those holding keys,
+// and where its records of one (row block, wave) start and step (shared by the
+// combine kernels). Sparse calls and single sequences know their records
+// without reading memory; only the count holding keys of a single sequence
+// depends on kv_lens. Several sequences read their record map first.
 template <bool kSparseMode>
 __device__ __forceinline__ void group_records(const MainArgs& a, int group, int rb, int wave,
-                                              int& n_active, int64_t& rec0, int64_t& rec_stride) {
-  const GroupInfo gi = group_info(a, group, kSparseMode);
+                                              int& n_plan, int& n_active, int64_t& rec0,
+                                              int64_t& rec_stride) {
   if (kSparseMode) {
-    n_active = min(a.num_splits, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
+    const int n_tiles = (a.topk + kTile - 1) / kTile;
+    n_active = min(a.num_splits, (n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
+    n_plan = n_active;
     rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
     rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
+  } else if (a.num_groups == 1) {
+    n_plan = a.split_slots;
+    n_active = dense_active(group_info(a, group, false).n_tiles, a.split_slots);
+    rec0 = (int64_t)rb * kWaves + wave;
+    rec_stride = (int64_t)a.row_blocks * kWaves;
   } else {
-    int slot0;
-    if (a.num_groups == 1) {
-      slot0 = 0;
-      n_active = dense_active(gi.n_tiles, a.split_slots);
-    } else {
-      const int2 m = a.ws_meta[group];  // written by the split kernel
-      slot0 = m.x;
-      n_active = m.y;
-    }
-    rec0 = ((int64_t)slot0 * a.row_blocks + rb) * kWaves + wave;
+    const int2 m = a.ws_meta[group];  // written by the split kernel
+    n_plan = n_active = m.y;
+    rec0 = ((int64_t)m.x * a.row_blocks + rb) * kWaves + wave;
     rec_stride = (int64_t)a.row_blocks * kWaves;
   }
 }
 
-// Two-stage combine, first stage: block = (wave record, chunk c of 32 splits,
-// 32-dim block) merges splits 32c .. 32c+31 into the chunk record
+// Two-stage combine, first stage: block = (wave record, chunk c of 16 splits,
+// 32-dim block) merges splits 16c .. 16c+15 into the chunk record
 // (record * part_chunks + c) of ws_part. A chunk past the group's splits
-// writes zero weights, so the second stage skips it.
+// writes zero weights, so the second stage skips it. (Chunks of 16 rather than
+// 32 give a T=1 decode over a 64k prefix, 205 splits of 64 rows, 416 blocks
+// instead of 224.)
 template <int MODE>
 __global__ void __launch_bounds__(256) mla_combine_part_kernel(MainArgs a) {
   constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
@@ -1162,36 +1174,82 @@ __global__ void __launch_bounds__(256) mla_combine_part_kernel(MainArgs a) {
   const int rb = rbg % a.row_blocks;
   const int group = rbg / a.row_blocks;
   if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;  // padding wave record
-  int n_active;
+  int n_plan, n_active;
   int64_t rec0, rec_stride;
-  group_records<kSparseMode>(a, group, rb, wave, n_active, rec0, rec_stride);
-  if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
+  group_records<kSparseMode>(a, group, rb, wave, n_plan, n_active, rec0, rec_stride);
   const int64_t prec = (int64_t)wrec * a.part_chunks + c;
   float* part = a.ws_part + prec * kRecElems;
   float* part_st = a.ws_part + (int64_t)a.num_groups * a.row_blocks * kWaves * a.part_chunks * kRecElems +
                    prec * (4 * kRowsPerWave);
-  const int n_c = min(32, n_active - 32 * c);
-  if (n_c <= 0) {
-    if (db == 0 && threadIdx.x < kRowsPerWave) {
-      part_st[threadIdx.x] = -__builtin_inff();
-      part_st[kRowsPerWave + threadIdx.x] = 0.f;
-      part_st[2 * kRowsPerWave + threadIdx.x] = -__builtin_inff();
-      part_st[3 * kRowsPerWave + threadIdx.x] = 0.f;
-    }
-    return;
+  const int n_c_plan = min(kPartSplits, n_plan - kPartSplits * c);  // >= 1 for c < part_chunks
+  const int n_c = min(kPartSplits, n_active - kPartSplits * c);
+  // n_active <= 1: the split kernel wrote this group's out/lse itself
+  const bool go = n_active > 1 && n_c > 0;
+  const int64_t r0 = rec0 + (int64_t)(kPartSplits * c) * rec_stride;
+  static_assert(kPartSplits == 16, "first-stage chunks are merged by the 8- and 16-split bodies");
+  const bool done =
+      n_c_plan <= 8
+          ? combine_rows<8>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c_plan, n_c, r0, rec_stride,
+                            part, part_st, go)
+          : combine_rows<16>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c_plan, n_c, r0, rec_stride,
+                             part, part_st, go);
+  if (!done && n_active > 1 && db == 0 && threadIdx.x < kRowsPerWave) {
+    // a chunk past the splits holding keys: zero weights
+    part_st[threadIdx.x] = -__builtin_inff();
+    part_st[kRowsPerWave + threadIdx.x] = 0.f;
+    part_st[2 * kRowsPerWave + threadIdx.x] = -__builtin_inff();
+    part_st[3 * kRowsPerWave + threadIdx.x] = 0.f;
   }
-  const int64_t r0 = rec0 + (int64_t)(32 * c) * rec_stride;
-  if (n_c <= 8)
-    combine_rows<8>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c, r0, rec_stride, part, part_st);
-  else if (n_c <= 16)
-    combine_rows<16>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c, r0, rec_stride, part, part_st);
-  else
-    combine_rows<32>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c, r0, rec_stride, part, part_st);
 }
 
 // Second stage: block = (wave record, 32-dim block); each thread merges the
 // chunks' sums of 4 dims of one row: out = sum_c 2^(mq_c - M) A_c / sum_c
 // 2^(mq_c - M) W_c, lse = log2 sum_c 2^(me_c) E_c (natural log on output).
+// All of a thread's loads (KCH chunks' statistics and sums; past the last chunk
+// they re-read it and the values go unused) are issued before any is used: one
+// memory round trip, where a loop that tested each chunk's weight before
+// loading its sum took one per chunk.
+template <int KCH>
+__device__ __forceinline__ void merge_chunks(const MainArgs& a, int n_load, int n_chunks, int64_t prec0,
+                                             const float* st0, int db, int qq, int lane,
+                                             float& mq, float& me, float& wsum, float& esum, f32x4& acc) {
+  float s_mq[KCH], s_w[KCH], s_me[KCH], s_e[KCH];
+  f32x4 v[KCH];
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    const int cc = min(c, n_load - 1);
+    const float* st = st0 + cc * 4 * kRowsPerWave;
+    s_mq[c] = st[0];
+    s_w[c] = st[kRowsPerWave];
+    s_me[c] = st[2 * kRowsPerWave];
+    s_e[c] = st[3 * kRowsPerWave];
+    v[c] = *reinterpret_cast<const f32x4*>(a.ws_part + (prec0 + cc) * kRecElems + ((db * 4 + qq) * 64 + lane) * 4);
+  }
+  mq = -__builtin_inff();
+  me = -__builtin_inff();
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    if (c < n_chunks) {
+      mq = fmaxf(mq, s_mq[c]);
+      me = fmaxf(me, s_me[c]);
+    }
+  }
+  acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  wsum = 0.f;
+  esum = 0.f;
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    if (c < n_chunks) {
+      if (s_e[c] > 0.f) esum += fast_exp2(s_me[c] - me) * s_e[c];
+      if (s_w[c] > 0.f) {
+        const float f = fast_exp2(s_mq[c] - mq);
+        wsum += f * s_w[c];
+        acc += f * v[c];
+      }
+    }
+  }
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(256) mla_combine_chunks_kernel(MainArgs a) {
   constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
@@ -1203,36 +1261,24 @@ __global__ void __launch_bounds__(256) mla_combine_chunks_kernel(MainArgs a) {
   const int rb = rbg % a.row_blocks;
   const int group = rbg / a.row_blocks;
   if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;
-  int n_active;
+  int n_plan, n_active;
   int64_t rec0, rec_stride;
-  group_records<kSparseMode>(a, group, rb, wave, n_active, rec0, rec_stride);
-  if (n_active <= 1) return;
-  const int n_chunks = min(a.part_chunks, (n_active + 31) / 32);
+  group_records<kSparseMode>(a, group, rb, wave, n_plan, n_active, rec0, rec_stride);
+  const int n_chunks = min(a.part_chunks, (n_active + kPartSplits - 1) / kPartSplits);
   const int t = threadIdx.x;
   const int lane = t & 63, qq = t >> 6, half = lane >> 5, l32 = lane & 31;
   const int64_t prec0 = (int64_t)wrec * a.part_chunks;
   const float* st0 = a.ws_part + (int64_t)a.num_groups * a.row_blocks * kWaves * a.part_chunks * kRecElems +
                      prec0 * (4 * kRowsPerWave) + l32;
-  float mq = -__builtin_inff(), me = -__builtin_inff();
-  for (int c = 0; c < n_chunks; ++c) {
-    mq = fmaxf(mq, st0[c * 4 * kRowsPerWave]);
-    me = fmaxf(me, st0[c * 4 * kRowsPerWave + 2 * kRowsPerWave]);
-  }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f, esum = 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
-    const float* st = st0 + c * 4 * kRowsPerWave;
-    const float wq = st[kRowsPerWave];
-    const float e = st[3 * kRowsPerWave];
-    if (e > 0.f) esum += fast_exp2(st[2 * kRowsPerWave] - me) * e;
-    if (wq > 0.f) {
-      const float f = fast_exp2(st[0] - mq);
-      wsum += f * wq;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_part + (prec0 + c) * kRecElems +
-                                                        ((db * 4 + qq) * 64 + lane) * 4);
-      acc += f * v;
-    }
-  }
+  float mq, me, wsum, esum;
+  f32x4 acc;
+  static_assert(kMaxPartChunks == 16, "chunk counts up to 16");
+  // all chunk records are read (the host-known count), then the ones holding keys merged
+  const int nl = a.part_chunks;
+  if (nl <= 4) merge_chunks<4>(a, nl, n_chunks, prec0, st0, db, qq, lane, mq, me, wsum, esum, acc);
+  else if (nl <= 8) merge_chunks<8>(a, nl, n_chunks, prec0, st0, db, qq, lane, mq, me, wsum, esum, acc);
+  else merge_chunks<16>(a, nl, n_chunks, prec0, st0, db, qq, lane, mq, me, wsum, esum, acc);
+  if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
   const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
   if (row >= a.rows_per_group) return;
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
@@ -1264,33 +1310,19 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   const int t = threadIdx.x;
   if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;  // padding wave record
 
-  const GroupInfo gi = group_info(a, group, kSparseMode);
-  int n_active;
+  int n_plan, n_active;
   int64_t rec0, rec_stride;  // record of split 0 of this (group, rb, wave); step per split
-  if (kSparseMode) {
-    n_active = min(a.num_splits, (gi.n_tiles + a.chunk_tiles - 1) / a.chunk_tiles);
-    rec0 = ((int64_t)group * a.row_blocks + rb) * kWaves + wave;
-    rec_stride = (int64_t)a.num_groups * a.row_blocks * kWaves;
-  } else {
-    int slot0;
-    if (a.num_groups == 1) {
-      slot0 = 0;
-      n_active = dense_active(gi.n_tiles, a.split_slots);
-    } else {
-      const int2 m = a.ws_meta[group];  // written by the split kernel
-      slot0 = m.x;
-      n_active = m.y;
-    }
-    rec0 = ((int64_t)slot0 * a.row_blocks + rb) * kWaves + wave;
-    rec_stride = (int64_t)a.row_blocks * kWaves;
-  }
-  if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
-  if (n_active <= 8)
-    combine_rows<8>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_active, rec0, rec_stride);
-  else if (n_active <= 16)
-    combine_rows<16>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_active, rec0, rec_stride);
+  group_records<kSparseMode>(a, group, rb, wave, n_plan, n_active, rec0, rec_stride);
+  // (n_active <= 1: the split kernel wrote this group's out/lse itself)
+  if (n_plan <= 8)
+    combine_rows<8>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_plan, n_active, rec0, rec_stride,
+                    nullptr, nullptr, n_active > 1);
+  else if (n_plan <= 16)
+    combine_rows<16>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_plan, n_active, rec0, rec_stride,
+                     nullptr, nullptr, n_active > 1);
   else
-    combine_rows<32>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_active, rec0, rec_stride);
+    combine_rows<32>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_plan, n_active, rec0, rec_stride,
+                     nullptr, nullptr, n_active > 1);
 }
 
 // ---------------------------------------------------------------------------

@@ -423,7 +423,7 @@ def test_reference_rises_several_times_in_a_split(gpu_lib):
 @pytest.mark.parametrize("layout", ["contig", "sparse"])
 def test_two_stage_combine_many_splits(gpu_lib, layout):
     """Groups of more than 32 splits (one sequence, or sparse tokens) merge in
-    two stages: chunks of 32 splits, then the chunks. Split counts of 33..79,
+    two stages: chunks of 16 splits, then the chunks. Split counts of 33..79,
     a last chunk of a single split, and a sequence shorter than the planned
     length (its last planned chunks hold no split) all match the oracle."""
     import dataclasses
