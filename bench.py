@@ -728,8 +728,10 @@ def measured_ceilings(dev, gather=None, settle_s=0.0):
     in-kernel stamps read), (b) a 256 MiB device-to-device copy (read + write
     bytes) and, when `gather` is given (a call that enqueues the library's
     row-gather probe, and returns its bytes when called with count=True), (c)
-    that gather. All are event-timed on the current stream. With settle_s, the
-    matrix-core probe first runs back to back for that many seconds."""
+    that gather. All are event-timed on the current stream, the copy over 4 and
+    the gather over 14 back-to-back launches (cycling over the input copies).
+    With settle_s, the matrix-core probe first runs back to back for that many
+    seconds."""
     import torch
 
     import speculative_decode_verify_mla_amd as mv
@@ -737,16 +739,20 @@ def measured_ceilings(dev, gather=None, settle_s=0.0):
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def best(fn, reps=5, warm=2, after=None):
+    def best(fn, reps=5, warm=2, after=None, batch=1):
+        """Best of `reps` timings of `batch` back-to-back calls, per call: a
+        short kernel timed alone between two events would include the launch
+        (several microseconds)."""
         for _ in range(warm):
             fn()
         t = float("inf")
         for _ in range(reps):
             e0.record(stream)
-            fn()
+            for _ in range(batch):
+                fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            t = min(t, e0.elapsed_time(e1) * 1e-3)
+            t = min(t, e0.elapsed_time(e1) * 1e-3 / batch)
             if after is not None:
                 after()
         return t
@@ -771,14 +777,14 @@ def measured_ceilings(dev, gather=None, settle_s=0.0):
     t_mfma = best(lambda: mv.probe_mfma_bf16(blocks, iters, sink, stream=stream), after=read_clock)
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
-    t_copy = best(lambda: dst.copy_(src))
+    t_copy = best(lambda: dst.copy_(src), batch=4)
     out = {"mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
            "probe_clock_GHz": round(max(clocks), 3) if clocks else None,
            "copy_GBps": round(2 * src.numel() / t_copy / 1e9, 1)}
     del src, dst, sink
     if gather is not None:
         nbytes = gather(count=True)
-        out["gather_GBps"] = round(nbytes / best(gather) / 1e9, 1)
+        out["gather_GBps"] = round(nbytes / best(gather, batch=14) / 1e9, 1)
     log(f"measured ceilings: {out}")
     return out
 
