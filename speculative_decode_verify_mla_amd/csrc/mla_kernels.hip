@@ -480,12 +480,15 @@ mla_split_kernel(MainArgs a) {
   int nv_cur = 0, nv_next = 0;
   uint64_t vm_cur = 0, vm_next = 0;
   int idx_next = -1;
+  // Sparse: the first tile's indices, fetched before the query rows' DMA so
+  // that their round trip overlaps it (a second pass fetches them again).
+  int idx_first = kSparseMode ? fetch_index(t_begin) : -1;
   auto issue_first_tile = [&]() {
     TileLoad tl0;
     nv_next = 0;
     vm_next = 0;
     if (kSparseMode) {
-      const int r0 = resolve_row(fetch_index(t_begin));
+      const int r0 = resolve_row(idx_first);
       vm_cur = __ballot(r0 >= 0);
       tl0 = prepare_sparse(r0, 0);
       idx_next = t_begin + 1 < t_end ? fetch_index(t_begin + 1) : -1;
@@ -722,6 +725,7 @@ mla_split_kernel(MainArgs a) {
     lq_run = 0.f;
     bool overflow = false;
 
+    if (kSparseMode && pass > 0) idx_first = fetch_index(t_begin);
     if (kSparseMode || pass > 0) issue_first_tile();  // stage 0 is free: a pass ends on a barrier
     if (q_after_gather && pass == 0) read_query();
     if (threadIdx.x == 0) *restart_flag = 0;
