@@ -247,6 +247,30 @@ def test_late_large_score_takes_exact_second_pass(gpu_lib):
         assert np.abs(out[0, 0] - synth.bf16_bits_to_f64(w.c_kv[j])).max() < 1e-2
 
 
+def test_sparse_late_large_score_takes_exact_second_pass(gpu_lib):
+    """The sparse path's second pass: the key at position 450 of token 0's index
+    list (8th 64-key tile) scores ~100 nats above the rest, more than the 2^96
+    a tile may grow past the exponent reference set by the split's first tile.
+    The split runs again, its first tile's indices fetched anew; the result is
+    that key's row, for one split, the automatic plan and three splits."""
+    spec = Spec("argmax_sparse", B=1, T=2, H=64, layout="sparse", cache_len=3000, topk=600)
+    w = generate(spec, seed=31)
+    j = int(w.indices[0, 0, 450])
+    m = int(np.searchsorted(w.row_ids, j))
+    assert w.row_ids[m] == j
+    kv = synth.bf16_bits_to_f32(w.c_kv[m])
+    c = 100.0 / (float(kv.astype(np.float64) @ kv) * w.scale)
+    w.q_lat[0, 0, :] = synth.f32_to_bf16_bits(np.broadcast_to(c * kv, (w.H, 512)).copy())
+    _announce("sparse late large score", w)
+    ref_out, ref_lse = run_oracle(w)
+    d = _dev(w)
+    for s in (1, 0, 3):
+        d.run(num_splits=s)
+        out, lse = d.results()
+        _check(out, lse, ref_out, ref_lse, tag=f"sparse argmax splits={s}")
+        assert np.abs(out[0, 0] - synth.bf16_bits_to_f64(w.c_kv[m])).max() < 1e-2
+
+
 def test_ragged_batch_with_empty_sequence(gpu_lib):
     """kv_lens of 0 in a batch: that sequence's rows are out = 0, lse = -inf; the
     device split plan still balances the others and they match the oracle."""
