@@ -531,17 +531,24 @@ mla_split_kernel(MainArgs a) {
     }
   }
   bf16x8 q[36];
-  auto read_query = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);  // the rows' DMA landed
+  auto read_query = [&](bool after_gather) {
+    // the rows' DMA landed (after a first gather, whose 18 loads and index
+    // prefetch went out later, only the rows' own: those loads may stay in flight)
+    if (after_gather) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else __builtin_amdgcn_s_waitcnt(0);
     if (wave_active) {
       // chunk 2c + h of latent row r sits at r*1024 + 16*((2c + h) ^ (r & 15)) =
       // (lb ^ 32*(c % 8)) + 256*(c / 8), lb = r*1024 + 16*(h ^ (r & 15)); rope
       // chunk 2j + h at rb ^ 32j, rb = 32768 + r*128 + 16*(h ^ ((r >> 1) & 7)).
-      // The bases are opaque here, so the compiler builds the 36 offsets at the
-      // reads instead of hoisting them to the prologue (and spilling them).
-      unsigned lb = (unsigned)(l32 * 1024 + 16 * (half ^ (l32 & 15)));
-      unsigned rbq = (unsigned)(kQLatBytes + l32 * 128 + 16 * (half ^ ((l32 >> 1) & 7)));
-      asm volatile("" : "+v"(lb), "+v"(rbq));
+      // Built here from the lane index counted anew (v_mbcnt, in an asm block
+      // the compiler cannot move), so the 36 offsets are computed at the reads
+      // instead of being hoisted (with their bases, or the lane index) to the
+      // prologue and spilled.
+      unsigned ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const unsigned r = ln & 31u, h = ln >> 5;
+      const unsigned lb = r * 1024u + 16u * (h ^ (r & 15u));
+      const unsigned rbq = (unsigned)kQLatBytes + r * 128u + 16u * (h ^ ((r >> 1) & 7u));
 #pragma unroll
       for (int c = 0; c < 36; ++c) {
         const unsigned off = c < 32 ? (lb ^ (unsigned)(32 * (c & 7))) + (unsigned)(256 * (c >> 3))
@@ -596,7 +603,7 @@ mla_split_kernel(MainArgs a) {
   // out (in the pass loop); the others now.
   const bool q_after_gather = kSparseMode && q_in_stage1;
   if (!q_after_gather) {
-    read_query();
+    read_query(false);
     if (!q_in_stage1) {
       __builtin_amdgcn_s_waitcnt(0);  // this wave's reads of both stages are done
       __syncthreads();                // ... and every other wave's
@@ -727,7 +734,7 @@ mla_split_kernel(MainArgs a) {
 
     if (kSparseMode && pass > 0) idx_first = fetch_index(t_begin);
     if (kSparseMode || pass > 0) issue_first_tile();  // stage 0 is free: a pass ends on a barrier
-    if (q_after_gather && pass == 0) read_query();
+    if (q_after_gather && pass == 0) read_query(true);
     if (threadIdx.x == 0) *restart_flag = 0;
 
     for (int tile = t_begin; tile < t_end; ++tile) {
