@@ -127,8 +127,7 @@ typedef struct mla_plan_info {
   int32_t num_groups;     /* query groups: B (dense) or B*T (sparse) */
   int32_t rows_per_group; /* T*H (dense) or H (sparse) */
   int32_t split_slots;    /* (group, split) slots per row block; the workspace holds
-                             split_slots * row_blocks * 4 records (and, for groups of
-                             more than 32 splits, the sums of a two-stage combine) */
+                             split_slots * row_blocks * 4 records */
   size_t workspace_bytes; /* device bytes the call needs; 0 when there is one slot in all */
 } mla_plan_info;
 

@@ -94,12 +94,10 @@ int check_device() {
   return st == 1 ? MLA_OK : MLA_ERR_UNSUPPORTED;
 }
 
-// Chunks of 16 splits for a two-stage combine: groups of more than 32 splits
-// whose split count the host knows (sparse calls: uniform; one dense sequence:
-// its slots); 0 = one-stage combine.
-int64_t plan_part_chunks(bool sparse, int64_t groups, int64_t splits) {
-  if (!(sparse || groups == 1) || splits <= mlav::kPartOneStageMax) return 0;
-  return ceil_div(splits, mlav::kPartSplits);
+// Groups of more than 32 splits whose split count the host knows (sparse calls:
+// uniform; one dense sequence: its slots) combine in the wide kernel.
+bool plan_wide_combine(bool sparse, int64_t groups, int64_t splits) {
+  return (sparse || groups == 1) && splits > mlav::kOneStageMaxSplits;
 }
 
 int make_plan(const mla_dims* d, bool sparse, mla_plan_info* p) {
@@ -163,14 +161,9 @@ int make_plan(const mla_dims* d, bool sparse, mla_plan_info* p) {
   p->split_slots = (int32_t)slots;
   // One slot in all: the split kernel writes out/lse directly, no workspace.
   const bool single = sparse ? splits == 1 : slots == 1;
-  // records, then (dense, several sequences) the per-sequence record map, then
-  // (groups of more than 32 splits whose count the host knows: sparse calls and
-  // single sequences) the chunk records of a two-stage combine
+  // records, then (dense, several sequences) the per-sequence record map
   const size_t meta = (!sparse && groups > 1) ? (size_t)groups * sizeof(int2) : 0;
-  const int64_t chunks = plan_part_chunks(sparse, groups, splits);
-  p->workspace_bytes = single ? 0
-                              : (size_t)slots * row_blocks * kWaves * mlav::kRecBytes + meta +
-                                    (size_t)(groups * row_blocks * kWaves * chunks) * mlav::kPartRecBytes;
+  p->workspace_bytes = single ? 0 : (size_t)slots * row_blocks * kWaves * mlav::kRecBytes + meta;
   return MLA_OK;
 }
 
@@ -264,9 +257,7 @@ int run(const mla_dims* d, bool sparse, const uint16_t* q_lat, const uint16_t* q
     a.ws_lse = reinterpret_cast<float*>(a.ws_o + records * mlav::kRecElems);
     if (!sparse && p.num_groups > 1)
       a.ws_meta = reinterpret_cast<int2*>(a.ws_lse + records * mlav::kRecRowStats * mlav::kRowsPerWave);
-    a.part_chunks = (int32_t)plan_part_chunks(sparse, p.num_groups, p.num_splits);
-    if (a.part_chunks > 0)  // (no record map here: sparse, or a single sequence)
-      a.ws_part = a.ws_lse + records * mlav::kRecRowStats * mlav::kRowsPerWave;
+    a.wide_combine = plan_wide_combine(sparse, p.num_groups, p.num_splits) ? 1 : 0;
   }
   a.kv_seq_stride = page_table ? 0 : d->kv_seq_stride;
   a.kv_rows = d->kv_rows;

@@ -28,13 +28,10 @@ constexpr int kMaxSplits = 256;  // per query group (combine weights live in LDS
 constexpr int kMinChunkDense = 2;
 constexpr int kMinChunkSparse = 4;
 constexpr size_t kRecBytes = (size_t)kRecElems * 2 + (size_t)kRecRowStats * kRowsPerWave * 4;
-// Two-stage combine (groups of more than 32 splits, when a group's split count
-// is known on the host): one chunk record per (wave record, 16 splits), an fp32
-// sum of 32 rows x 512 dims plus 4 floats per row.
-constexpr int kPartSplits = 16;
-constexpr int kPartOneStageMax = 32;  // up to this many splits a group combines in one stage
-constexpr int kMaxPartChunks = kMaxSplits / kPartSplits;
-constexpr size_t kPartRecBytes = (size_t)kRecElems * 4 + (size_t)4 * kRowsPerWave * 4;
+// Groups of more than this many splits, whose split count the host knows
+// (sparse calls, single sequences), combine in the wide kernel: one workgroup
+// per 32 rows x 8 dims with every split's loads in flight at once.
+constexpr int kOneStageMaxSplits = 32;
 
 enum Mode : int { kContig = 0, kPaged = 1, kSparse = 2, kSparsePaged = 3 };
 
@@ -52,8 +49,6 @@ struct MainArgs {
   uint16_t* ws_o; // [records][16384] fp16, register-native order
   float* ws_lse;  // [records][3][32] fp32: lse2 (fp32 terms), lse2 (rounded terms), scale
   int2* ws_meta;  // dense: [groups] (first slot, splits holding keys), written by the split kernel
-  float* ws_part; // two-stage combine: [records x part_chunks][16384] fp32 chunk sums, then
-                  // [records x part_chunks][4][32] per-row chunk statistics
   int64_t kv_seq_stride;
   int64_t kv_rows;
   int32_t T, H;
@@ -70,7 +65,7 @@ struct MainArgs {
   int32_t slot_stride;  // dense: workgroups per row block in the grid (= split_slots)
   int32_t fixed_chunk;  // dense: tiles per split when requested, 0 = chosen on the device
   int32_t final_out;    // 1: single split for every group, write out/lse directly
-  int32_t part_chunks;  // > 0: combine in two stages over chunks of 16 splits (groups of > 32 splits)
+  int32_t wide_combine;  // != 0: groups of more than 32 splits (sparse, or one sequence): wide combine
   float scale_log2;    // scale * log2(e)
 };
 

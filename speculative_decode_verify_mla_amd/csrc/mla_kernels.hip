@@ -983,18 +983,12 @@ static_assert(16 * 256 * 4 == kRecElems, "16 combine blocks of 256 threads x 4 d
 // count n_active <= n_plan, which depends on kv_lens, is used: the kv_lens
 // round trip overlaps the workspace loads. A block whose group ended up with
 // one split (written out by the split kernel itself) returns after the loads.
-// With `part` (the first stage of a two-stage combine, for groups of more than
-// 32 splits): the block merges only its chunk of splits and writes, instead of
-// out/lse, the chunk's unnormalised fp32 sum (part, register-native order) and
-// per row its log2 maxima and sums (part_st: max of the rounded-term log2
-// sums, their weight sum, max of the fp32-term ones, their sum).
 template <int KBATCH>
 __device__ __forceinline__ bool combine_rows(const MainArgs& a, float (*wts)[kMaxSplits + 1],
                                              float (*red)[8][kRowsPerWave], float* row_lse,
                                              float* row_inv, int rb, int group, int wave, int db,
                                              int n_plan, int n_active, int64_t rec0, int64_t rec_stride,
-                                             float* part = nullptr, float* part_st = nullptr,
-                                             bool go = true) {
+                                             bool go) {
   constexpr int kBatch = KBATCH;
   const int t = threadIdx.x;
   const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
@@ -1084,12 +1078,6 @@ __device__ __forceinline__ bool combine_rows(const MainArgs& a, float (*wts)[kMa
     if (sl == 0) row_inv[r] = ws > 0.f ? 1.0f / ws : 0.f;
     if (sl == 0)
       row_lse[r] = (mx != -__builtin_inff() && es > 0.f) ? (mx + fast_log2(es)) * kLn2 : -__builtin_inff();
-    if (part_st != nullptr && sl == 0 && db == 0) {
-      part_st[r] = mxq;
-      part_st[kRowsPerWave + r] = ws;
-      part_st[2 * kRowsPerWave + r] = mx;
-      part_st[3 * kRowsPerWave + r] = es;
-    }
     __syncthreads();
   }
 
@@ -1112,10 +1100,6 @@ __device__ __forceinline__ bool combine_rows(const MainArgs& a, float (*wts)[kMa
         acc[3] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].y >> 16));
       }
     }
-  }
-  if (part != nullptr) {
-    *reinterpret_cast<f32x4*>(part + ((db * 4 + qq) * 64 + lane) * 4) = acc;
-    return true;
   }
   if (row >= a.rows_per_group) return true;
   const float inv = row_inv[l32];
@@ -1161,25 +1145,135 @@ __device__ __forceinline__ void group_records(const MainArgs& a, int group, int 
   }
 }
 
-// Two-stage combine, first stage: block = (wave record, chunk c of 16 splits,
-// 32-dim block) merges splits 16c .. 16c+15 into the chunk record
-// (record * part_chunks + c) of ws_part. A chunk past the group's splits
-// writes zero weights, so the second stage skips it. (Chunks of 16 rather than
-// 32 give a T=1 decode over a 64k prefix, 205 splits of 64 rows, 416 blocks
-// instead of 224.)
+// Combine for groups of more than 32 splits (sparse calls and single
+// sequences, whose split count is planned on the host), in one launch: block =
+// (wave record, 8-dim group g = 4 db + qq), i.e. 32 rows x 8 dims, the 512
+// contiguous bytes of every split's record that hold them; 512 threads = 8
+// split groups x 64 lanes (row l32, dims 4h .. 4h+3). Each thread issues the
+// loads of its splits' partials (sg, sg + 8, ...; at most KPT) before anything
+// else, phase 1 turns the statistics (16 split lanes per row) into weights in
+// LDS meanwhile, each split group accumulates its splits, and the 8 sums meet in
+// LDS: one memory round trip in all, where the two-stage combine took two
+// launches with two round trips each and measured slower (workload 6: call
+// 39.5 against 37.6 us).
+constexpr int kWideThreads = 512;
+constexpr int kWideGroups = kWideThreads / 64;  // split groups
+template <int KPT>
+__device__ __forceinline__ void combine_wide(const MainArgs& a, float (*wts)[kMaxSplits + 1],
+                                             float (*red)[16][kRowsPerWave], f32x4 (*gsum)[64],
+                                             float* row_lse, float* row_inv, int g, int rb, int group,
+                                             int wave, int n_plan, int n_active, int64_t rec0,
+                                             int64_t rec_stride) {
+  const int t = threadIdx.x;
+  const int sg = t >> 6, lane = t & 63, half = lane >> 5, l32 = lane & 31;
+  const uint16_t* o_p = a.ws_o + rec0 * kRecElems + (g * 64 + lane) * 4;
+  const int64_t o_step = rec_stride * kRecElems;
+  uint2 raw[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    raw[j] = *reinterpret_cast<const uint2*>(o_p + min(sg + kWideGroups * j, n_plan - 1) * o_step);
+  // the statistics of splits sl, sl + 16, ... (phase 1: thread = row r x split
+  // lane sl; at most KPT / 2 each), read once (loading them before the partials
+  // measured slower)
+  const int r = t & 31, sl = t >> 5;  // 16 split lanes per row
+  const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
+  const float* st = a.ws_lse + rec0 * (kRecRowStats * kRowsPerWave) + r;
+  constexpr int KST = KPT / 2;
+  float h_le[KST], h_lq[KST], h_sc[KST];
+#pragma unroll
+  for (int i = 0; i < KST; ++i) {
+    const int sc = min(sl + 16 * i, n_plan - 1);
+    h_le[i] = st[sc * st_step];
+    h_lq[i] = st[sc * st_step + kRowsPerWave];
+    h_sc[i] = st[sc * st_step + 2 * kRowsPerWave];
+  }
+  if (n_active <= 1) return;  // (block-uniform) the split kernel wrote out/lse itself
+
+  // ---- phase 1: per-row maxima, sums and weights ---------------------------------
+  float mx = -__builtin_inff(), mxq = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < KST; ++i) {
+    if (sl + 16 * i < n_active) {
+      mx = fmaxf(mx, h_le[i]);
+      mxq = fmaxf(mxq, h_lq[i]);
+    }
+  }
+  red[0][sl][r] = mx;
+  red[1][sl][r] = mxq;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    mx = fmaxf(mx, red[0][j][r]);
+    mxq = fmaxf(mxq, red[1][j][r]);
+  }
+  __syncthreads();
+  float es = 0.f, ws = 0.f;
+#pragma unroll
+  for (int i = 0; i < KST; ++i) {
+    const int s = sl + 16 * i;
+    if (s < n_active) {
+      const float w = h_lq[i] == -__builtin_inff() ? 0.f : fast_exp2(h_lq[i] - mxq);
+      es += h_le[i] == -__builtin_inff() ? 0.f : fast_exp2(h_le[i] - mx);
+      ws += w;
+      wts[r][s] = w * h_sc[i];
+    }
+  }
+  red[0][sl][r] = es;
+  red[1][sl][r] = ws;
+  __syncthreads();
+  if (sl == 0) {
+    es = 0.f;
+    ws = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      es += red[0][j][r];
+      ws += red[1][j][r];
+    }
+    row_inv[r] = ws > 0.f ? 1.0f / ws : 0.f;
+    row_lse[r] = (mx != -__builtin_inff() && es > 0.f) ? (mx + fast_log2(es)) * kLn2 : -__builtin_inff();
+  }
+
+  // ---- phase 2: this split group's weighted sum of 4 dims of one row -------------
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int s = sg + kWideGroups * j;
+    if (s < n_active) {
+      const float w = wts[l32][s];
+      acc[0] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].x & 0xffffu));
+      acc[1] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].x >> 16));
+      acc[2] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].y & 0xffffu));
+      acc[3] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].y >> 16));
+    }
+  }
+  if (sg > 0) gsum[sg - 1][lane] = acc;
+  __syncthreads();
+  if (sg > 0) return;
+#pragma unroll
+  for (int j = 0; j < kWideGroups - 1; ++j) acc += gsum[j][lane];
+  const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
+  if (row >= a.rows_per_group) return;
+  const float inv = row_inv[l32];
+  const int64_t qrow = (int64_t)group * a.rows_per_group + row;
+  const int d = (g >> 2) * 32 + 8 * (g & 3) + 4 * half;
+  uint2 pkd;
+  pkd.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pkd.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
+  if (g == 0 && half == 0) a.lse[qrow] = row_lse[l32];
+}
+
 template <int MODE>
-__global__ void __launch_bounds__(256) mla_combine_part_kernel(MainArgs a) {
+__global__ void __launch_bounds__(kWideThreads) mla_combine_wide_kernel(MainArgs a) {
   constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
-  __shared__ float wts[kRowsPerWave][kMaxSplits + 1];
-  __shared__ float red[3][8][kRowsPerWave];
+  __shared__ float wts[kRowsPerWave][kMaxSplits + 1];  // unnormalised weight x fp16 scale
+  __shared__ float red[2][16][kRowsPerWave];
+  __shared__ f32x4 gsum[kWideGroups - 1][64];
   __shared__ float row_lse[kRowsPerWave];
   __shared__ float row_inv[kRowsPerWave];
-
   const int bid = blockIdx.x;
-  const int db = bid & 15;
-  const int rest = bid >> 4;
-  const int c = rest % a.part_chunks;
-  const int wrec = rest / a.part_chunks;
+  const int g = bid & 63;
+  const int wrec = bid >> 6;
   const int wave = wrec & 3;
   const int rbg = wrec >> 2;
   const int rb = rbg % a.row_blocks;
@@ -1188,119 +1282,13 @@ __global__ void __launch_bounds__(256) mla_combine_part_kernel(MainArgs a) {
   int n_plan, n_active;
   int64_t rec0, rec_stride;
   group_records<kSparseMode>(a, group, rb, wave, n_plan, n_active, rec0, rec_stride);
-  const int64_t prec = (int64_t)wrec * a.part_chunks + c;
-  float* part = a.ws_part + prec * kRecElems;
-  float* part_st = a.ws_part + (int64_t)a.num_groups * a.row_blocks * kWaves * a.part_chunks * kRecElems +
-                   prec * (4 * kRowsPerWave);
-  const int n_c_plan = min(kPartSplits, n_plan - kPartSplits * c);  // >= 1 for c < part_chunks
-  const int n_c = min(kPartSplits, n_active - kPartSplits * c);
-  // n_active <= 1: the split kernel wrote this group's out/lse itself
-  const bool go = n_active > 1 && n_c > 0;
-  const int64_t r0 = rec0 + (int64_t)(kPartSplits * c) * rec_stride;
-  static_assert(kPartSplits == 16, "first-stage chunks are merged by the 8- and 16-split bodies");
-  const bool done =
-      n_c_plan <= 8
-          ? combine_rows<8>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c_plan, n_c, r0, rec_stride,
-                            part, part_st, go)
-          : combine_rows<16>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_c_plan, n_c, r0, rec_stride,
-                             part, part_st, go);
-  if (!done && n_active > 1 && db == 0 && threadIdx.x < kRowsPerWave) {
-    // a chunk past the splits holding keys: zero weights
-    part_st[threadIdx.x] = -__builtin_inff();
-    part_st[kRowsPerWave + threadIdx.x] = 0.f;
-    part_st[2 * kRowsPerWave + threadIdx.x] = -__builtin_inff();
-    part_st[3 * kRowsPerWave + threadIdx.x] = 0.f;
-  }
-}
-
-// Second stage: block = (wave record, 32-dim block); each thread merges the
-// chunks' sums of 4 dims of one row: out = sum_c 2^(mq_c - M) A_c / sum_c
-// 2^(mq_c - M) W_c, lse = log2 sum_c 2^(me_c) E_c (natural log on output).
-// All of a thread's loads (KCH chunks' statistics and sums; past the last chunk
-// they re-read it and the values go unused) are issued before any is used: one
-// memory round trip, where a loop that tested each chunk's weight before
-// loading its sum took one per chunk.
-template <int KCH>
-__device__ __forceinline__ void merge_chunks(const MainArgs& a, int n_load, int n_chunks, int64_t prec0,
-                                             const float* st0, int db, int qq, int lane,
-                                             float& mq, float& me, float& wsum, float& esum, f32x4& acc) {
-  float s_mq[KCH], s_w[KCH], s_me[KCH], s_e[KCH];
-  f32x4 v[KCH];
-#pragma unroll
-  for (int c = 0; c < KCH; ++c) {
-    const int cc = min(c, n_load - 1);
-    const float* st = st0 + cc * 4 * kRowsPerWave;
-    s_mq[c] = st[0];
-    s_w[c] = st[kRowsPerWave];
-    s_me[c] = st[2 * kRowsPerWave];
-    s_e[c] = st[3 * kRowsPerWave];
-    v[c] = *reinterpret_cast<const f32x4*>(a.ws_part + (prec0 + cc) * kRecElems + ((db * 4 + qq) * 64 + lane) * 4);
-  }
-  mq = -__builtin_inff();
-  me = -__builtin_inff();
-#pragma unroll
-  for (int c = 0; c < KCH; ++c) {
-    if (c < n_chunks) {
-      mq = fmaxf(mq, s_mq[c]);
-      me = fmaxf(me, s_me[c]);
-    }
-  }
-  acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  wsum = 0.f;
-  esum = 0.f;
-#pragma unroll
-  for (int c = 0; c < KCH; ++c) {
-    if (c < n_chunks) {
-      if (s_e[c] > 0.f) esum += fast_exp2(s_me[c] - me) * s_e[c];
-      if (s_w[c] > 0.f) {
-        const float f = fast_exp2(s_mq[c] - mq);
-        wsum += f * s_w[c];
-        acc += f * v[c];
-      }
-    }
-  }
-}
-
-template <int MODE>
-__global__ void __launch_bounds__(256) mla_combine_chunks_kernel(MainArgs a) {
-  constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
-  const int bid = blockIdx.x;
-  const int db = bid & 15;
-  const int wrec = bid >> 4;
-  const int wave = wrec & 3;
-  const int rbg = wrec >> 2;
-  const int rb = rbg % a.row_blocks;
-  const int group = rbg / a.row_blocks;
-  if (rb * kRowsPerBlock + wave * kRowsPerWave >= a.rows_per_group) return;
-  int n_plan, n_active;
-  int64_t rec0, rec_stride;
-  group_records<kSparseMode>(a, group, rb, wave, n_plan, n_active, rec0, rec_stride);
-  const int n_chunks = min(a.part_chunks, (n_active + kPartSplits - 1) / kPartSplits);
-  const int t = threadIdx.x;
-  const int lane = t & 63, qq = t >> 6, half = lane >> 5, l32 = lane & 31;
-  const int64_t prec0 = (int64_t)wrec * a.part_chunks;
-  const float* st0 = a.ws_part + (int64_t)a.num_groups * a.row_blocks * kWaves * a.part_chunks * kRecElems +
-                     prec0 * (4 * kRowsPerWave) + l32;
-  float mq, me, wsum, esum;
-  f32x4 acc;
-  static_assert(kMaxPartChunks == 16, "chunk counts up to 16");
-  // all chunk records are read (the host-known count), then the ones holding keys merged
-  const int nl = a.part_chunks;
-  if (nl <= 4) merge_chunks<4>(a, nl, n_chunks, prec0, st0, db, qq, lane, mq, me, wsum, esum, acc);
-  else if (nl <= 8) merge_chunks<8>(a, nl, n_chunks, prec0, st0, db, qq, lane, mq, me, wsum, esum, acc);
-  else merge_chunks<16>(a, nl, n_chunks, prec0, st0, db, qq, lane, mq, me, wsum, esum, acc);
-  if (n_active <= 1) return;  // the split kernel wrote this group's out/lse itself
-  const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
-  if (row >= a.rows_per_group) return;
-  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  const int64_t qrow = (int64_t)group * a.rows_per_group + row;
-  const int d = db * 32 + 8 * qq + 4 * half;
-  uint2 pkd;
-  pkd.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  pkd.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
-  if (db == 0 && qq == 0 && half == 0)
-    a.lse[qrow] = (me != -__builtin_inff() && esum > 0.f) ? (me + fast_log2(esum)) * kLn2 : -__builtin_inff();
+  static_assert(kWideGroups * 32 >= kMaxSplits, "one batch of loads covers every split");
+  if (n_plan <= kWideGroups * 8)
+    combine_wide<8>(a, wts, red, gsum, row_lse, row_inv, g, rb, group, wave, n_plan, n_active, rec0, rec_stride);
+  else if (n_plan <= kWideGroups * 16)
+    combine_wide<16>(a, wts, red, gsum, row_lse, row_inv, g, rb, group, wave, n_plan, n_active, rec0, rec_stride);
+  else
+    combine_wide<32>(a, wts, red, gsum, row_lse, row_inv, g, rb, group, wave, n_plan, n_active, rec0, rec_stride);
 }
 
 template <int MODE>
@@ -1327,13 +1315,13 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
   // (n_active <= 1: the split kernel wrote this group's out/lse itself)
   if (n_plan <= 8)
     combine_rows<8>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_plan, n_active, rec0, rec_stride,
-                    nullptr, nullptr, n_active > 1);
+                    n_active > 1);
   else if (n_plan <= 16)
     combine_rows<16>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_plan, n_active, rec0, rec_stride,
-                     nullptr, nullptr, n_active > 1);
+                     n_active > 1);
   else
     combine_rows<32>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_plan, n_active, rec0, rec_stride,
-                     nullptr, nullptr, n_active > 1);
+                     n_active > 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1350,12 +1338,8 @@ static hipError_t launch_split(const MainArgs& a, hipStream_t s) {
 template <int MODE>
 static hipError_t launch_combine(const MainArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)a.num_groups * (unsigned)a.row_blocks * kWaves * 16u;
-  if (a.part_chunks > 0) {
-    hipLaunchKernelGGL(mla_combine_part_kernel<MODE>, dim3(grid * (unsigned)a.part_chunks), dim3(256),
-                       0, s, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mla_combine_chunks_kernel<MODE>, dim3(grid), dim3(256), 0, s, a);
+  if (a.wide_combine) {
+    hipLaunchKernelGGL(mla_combine_wide_kernel<MODE>, dim3(grid * 4u), dim3(kWideThreads), 0, s, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(mla_combine_kernel<MODE>, dim3(grid), dim3(256), 0, s, a);

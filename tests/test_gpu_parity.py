@@ -451,16 +451,17 @@ def test_reference_rises_several_times_in_a_split(gpu_lib):
 
 
 @pytest.mark.parametrize("layout", ["contig", "sparse"])
-def test_two_stage_combine_many_splits(gpu_lib, layout):
-    """Groups of more than 32 splits (one sequence, or sparse tokens) merge in
-    two stages: chunks of 16 splits, then the chunks. Split counts of 33..79,
-    a last chunk of a single split, and a sequence shorter than the planned
-    length (its last planned chunks hold no split) all match the oracle."""
+def test_many_splits_combine(gpu_lib, layout):
+    """Groups of more than 32 splits (one sequence, or sparse tokens) combine in
+    the wide kernel (every split's loads of 32 rows x 8 dims in flight at once,
+    8 split groups summed in LDS). Split counts of 33..79 and a sequence
+    shorter than the planned length (its last planned splits hold no key) all
+    match the oracle."""
     import dataclasses
     if layout == "contig":
         spec = Spec("many_splits", B=1, T=2, H=64, layout="contig", prefix=5000)
         w = generate(spec, seed=28)
-        _announce("two-stage combine, one sequence", w)
+        _announce("wide combine, one sequence", w)
         d = _dev(w)
         ref = run_oracle(w)
         for splits in (33, 60, 65, 79):
@@ -477,7 +478,7 @@ def test_two_stage_combine_many_splits(gpu_lib, layout):
         spec = Spec("many_splits_sparse", B=2, T=2, H=64, layout="sparse", cache_len=9000,
                     topk=3000)
         w = generate(spec, seed=29)
-        _announce("two-stage combine, sparse", w)
+        _announce("wide combine, sparse", w)
         d = _dev(w)
         ref = run_oracle(w)
         for splits in (33, 47):
