@@ -187,14 +187,15 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3,
-                    help="workload 1..5 (3 = the headline); 6 = the single-token decode "
-                         "diagnostic over the 64k prefix")
+                    help="workload of synth.CONFIGS: 1 tiny chain, 2 Kimi-K2-like (4k prefix), "
+                         "3 long prefix (64k, the headline), 4 batched paged, 5 sparse top-k, "
+                         "6 single-token decode over the 64k prefix")
     ap.add_argument("--copies", type=int, default=0,
                     help="input copies cycled through so repeats miss the 256 MB Infinity Cache "
                          "(0 = enough for twice its size, at least 4)")
     ap.add_argument("--splits", type=int, default=0, help="0 = library's automatic plan")
     ap.add_argument("--spike", type=float, default=0.0,
-                    help="workload 3 only: plant, in the last tile of every split, a key scoring "
+                    help="long-prefix workload only: plant, in the last tile of every split, a key scoring "
                          "this many nats above the rest for every query row (0 = off)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -250,7 +251,7 @@ def main():
     spiked = None
     if args.spike > 0:
         if args.config != 3:
-            raise SystemExit("--spike applies to workload 3 only")
+            raise SystemExit("--spike applies to the long-prefix workload (--config 3) only")
         w, spiked = plant_spikes(w, args, args.spike)
     wm = work_model(w)
     log(f"workload {w.spec.name}{' (spiked)' if spiked else ''}: B={w.B} T={w.T} H={w.H} "
@@ -271,7 +272,7 @@ def main():
     # which also takes the GPU out of its idle clock state, so the timed calls run
     # at the clock a busy GPU holds (from idle, the first few ms of calls run at
     # ~1.5 GHz instead of ~1.85: 20 calls after 5 warm-up calls measured 161.5
-    # instead of 151.3 us on workload 3) -----------------------------------------
+    # instead of 151.3 us on the long-prefix workload) --------------------------
     gather = vc.gather_probe() if w.layout == "sparse" else None
     ceil = measured_ceilings(dev, gather, settle_s=SETTLE_S)
     # host-side gaps of a few ms (allocations, syncs, Python) let the clock fall
@@ -946,7 +947,8 @@ def bench_proj(args, dev):
 
 def bench_topk(args, dev):
     """Top-k selection over one score per cached position, for every query token
-    of the sparse workload (default config 5: 32 tokens x 131,072, k = 2048)."""
+    of the sparse workload (by default the sparse top-k one: 32 tokens x 131,072,
+    k = 2048)."""
     import numpy as np
     import torch
 

@@ -313,8 +313,8 @@ CONFIGS = {
     # sparse top-k decode over a 131072-token cache
     5: Spec("sparse_b32_h64_k2048_l131072", B=32, T=1, H=64, layout="sparse",
             cache_len=131072, topk=2048),
-    # diagnostic (not one of the five): workload 3 with a single query token, a
-    # plain decode step over the 64k latent prefix, bound by reading the cache
+    # diagnostic (not one of the five): the long-prefix shape with a single query
+    # token, a plain decode step over the 64k latent prefix, bound by reading the cache
     6: Spec("decode_t1_h64_l65536", B=1, T=1, H=64, layout="contig", prefix=65536),
 }
 
