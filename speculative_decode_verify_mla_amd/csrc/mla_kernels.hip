@@ -934,6 +934,9 @@ mla_split_kernel(MainArgs a) {
     const int64_t rec = rec_slot * kWaves + wave;
     // fp16 with a per-row power-of-two scale keeps 11 significant bits of the
     // normalised partial (|o| <= the largest value-row entry) at half the bytes.
+    // The partials are stored non-temporally: every workgroup writes its
+    // 128 KB at the same moment and only the combine reads them, so they
+    // should not take L2 lines on their way out.
     float amax = 0.f;
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
@@ -949,10 +952,9 @@ mla_split_kernel(MainArgs a) {
     for (int db = 0; db < 16; ++db) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        uint2 pkd;
-        pkd.x = scale_pack_f16x2(o[db][4 * qq + 0], o[db][4 * qq + 1], inv_s);
-        pkd.y = scale_pack_f16x2(o[db][4 * qq + 2], o[db][4 * qq + 3], inv_s);
-        *reinterpret_cast<uint2*>(dst + ((db * 4 + qq) * 64 + lane) * 4) = pkd;
+        const u32x2 pkd = {scale_pack_f16x2(o[db][4 * qq + 0], o[db][4 * qq + 1], inv_s),
+                           scale_pack_f16x2(o[db][4 * qq + 2], o[db][4 * qq + 3], inv_s)};
+        __builtin_nontemporal_store(pkd, reinterpret_cast<u32x2*>(dst + ((db * 4 + qq) * 64 + lane) * 4));
       }
     }
     if (half == 0) {
@@ -976,7 +978,7 @@ mla_split_kernel(MainArgs a) {
 // ---------------------------------------------------------------------------
 static_assert(16 * 256 * 4 == kRecElems, "16 combine blocks of 256 threads x 4 dims cover one wave record");
 
-// The combine of one block; KBATCH (8, 16, 32) is the number of splits whose
+// The combine of one block; KBATCH (8, 16, 24, 32) is the number of splits whose
 // loads are issued together, chosen from the planned count n_plan so that a
 // block with few splits issues no loads it does not use. The loads are clamped
 // to the planned splits (whose records exist) and issued before the actual
@@ -1318,6 +1320,9 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MainArgs a) {
                     n_active > 1);
   else if (n_plan <= 16)
     combine_rows<16>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_plan, n_active, rec0, rec_stride,
+                     n_active > 1);
+  else if (n_plan <= 24)
+    combine_rows<24>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_plan, n_active, rec0, rec_stride,
                      n_active > 1);
   else
     combine_rows<32>(a, wts, red, row_lse, row_inv, rb, group, wave, db, n_plan, n_active, rec0, rec_stride,
