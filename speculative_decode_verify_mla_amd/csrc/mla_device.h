@@ -38,9 +38,13 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* __restrict__ base, 
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
 }
 
+// 16 bytes per lane from a buffer straight into LDS. kNonTemporal sets the
+// load's nt cache-policy bit (rows that no other workgroup will read).
+template <bool kNonTemporal = false>
 __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds_dst,
                                               unsigned voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(lds_dst), 16, voffset, 0, 0, 0);
+  constexpr int kPolicy = kNonTemporal ? 2 : 0;  // gfx950 cache-policy bits: nt = 2
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(lds_dst), 16, voffset, 0, 0, kPolicy);
 }
 
 // Buffer descriptors are wave-uniform; readfirstlane keeps them in SGPRs even

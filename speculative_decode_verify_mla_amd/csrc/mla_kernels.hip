@@ -398,7 +398,9 @@ mla_split_kernel(MainArgs a) {
 
   // A tile's 18 loads of this wave (16 latent key rows, 2 x 8 rope rows),
   // prepared once and issued one at a time: spread over the first score chain,
-  // they keep the vector-memory issue from stalling the wave.
+  // they keep the vector-memory issue from stalling the wave. Sparse gathers
+  // are non-temporal: a gathered row feeds one workgroup, whereas a dense tile
+  // is read by every row block of its chunk through the same L2.
   struct TileLoad {
     __amdgpu_buffer_rsrc_t rl, rr;
     uint8_t* dst;
@@ -458,7 +460,7 @@ mla_split_kernel(MainArgs a) {
       } else {
         off = (tl.lane16 ^ (unsigned)(16 * swz_lat(key & 15))) + (unsigned)key * 1024u;
       }
-      buffer_to_lds(tl.rl, tl.dst + key * 1024, off);
+      buffer_to_lds<kSparseMode>(tl.rl, tl.dst + key * 1024, off);
     } else {
       const int j = wave + 4 * (i - 16);
       unsigned off;
@@ -468,7 +470,7 @@ mla_split_kernel(MainArgs a) {
       } else {
         off = (unsigned)j * 1024u + (unsigned)((lane >> 3) * 128) + rope_chunk_off;
       }
-      buffer_to_lds(tl.rr, tl.dst + kLatBytes + j * 1024, off);
+      buffer_to_lds<kSparseMode>(tl.rr, tl.dst + kLatBytes + j * 1024, off);
     }
   };
   constexpr int kLoadsPerWave = 18;
@@ -1020,12 +1022,16 @@ __device__ __forceinline__ bool combine_rows(const MainArgs& a, float (*wts)[kMa
     h_lq[i] = v ? lq : -__builtin_inff();
     h_sc[i] = v ? sf : 0.f;
   }
+  // The partials are read once: non-temporal loads keep them out of the caches.
   const uint16_t* o_p = a.ws_o + rec0 * kRecElems + ((db * 4 + qq) * 64 + lane) * 4;
   const int64_t o_step = rec_stride * kRecElems;
+  auto load_partial = [&](int s) -> uint2 {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(o_p + s * o_step));
+    return uint2{v.x, v.y};
+  };
   uint2 raw[kBatch];
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j)
-    raw[j] = *reinterpret_cast<const uint2*>(o_p + min(j, n_plan - 1) * o_step);
+  for (int j = 0; j < kBatch; ++j) raw[j] = load_partial(min(j, n_plan - 1));
   if (!go || n_active < 1) return false;  // (block-uniform)
 
   // ---- phase 1: per-row maxima, sums and weights (thread = row x split lane) ----
@@ -1090,7 +1096,7 @@ __device__ __forceinline__ bool combine_rows(const MainArgs& a, float (*wts)[kMa
     if (s0 > 0) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j)
-        raw[j] = s0 + j < n_active ? *reinterpret_cast<const uint2*>(o_p + (s0 + j) * o_step) : uint2{0u, 0u};
+        raw[j] = s0 + j < n_active ? load_partial(s0 + j) : uint2{0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
