@@ -47,6 +47,14 @@ __device__ __forceinline__ void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint8
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(lds_dst), 16, voffset, 0, 0, kPolicy);
 }
 
+// 8 bytes per lane stored through a buffer descriptor with the sc0 and sc1
+// cache-policy bits set (system scope: written through the caches rather than
+// left dirty in L2 at the kernel's end).
+__device__ __forceinline__ void buffer_store_b64_wt(u32x2 v, __amdgpu_buffer_rsrc_t rsrc, unsigned voffset) {
+  constexpr int kPolicy = 1 | 16;  // gfx950 cache-policy bits: sc0 = 1, sc1 = 16
+  __builtin_amdgcn_raw_buffer_store_b64(v, rsrc, (int)voffset, 0, kPolicy);
+}
+
 // Buffer descriptors are wave-uniform; readfirstlane keeps them in SGPRs even
 // when the compiler cannot prove uniformity (it would otherwise emit a loop).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

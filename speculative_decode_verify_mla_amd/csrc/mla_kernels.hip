@@ -936,9 +936,10 @@ mla_split_kernel(MainArgs a) {
     const int64_t rec = rec_slot * kWaves + wave;
     // fp16 with a per-row power-of-two scale keeps 11 significant bits of the
     // normalised partial (|o| <= the largest value-row entry) at half the bytes.
-    // The partials are stored non-temporally: every workgroup writes its
-    // 128 KB at the same moment and only the combine reads them, so they
-    // should not take L2 lines on their way out.
+    // The partials are written through the caches (sc0 sc1 stores): every
+    // workgroup writes its 128 KB at the same moment and only the combine, a
+    // later kernel, reads them, so they should neither take L2 lines nor be
+    // left dirty there for the kernel's end.
     float amax = 0.f;
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
@@ -949,14 +950,14 @@ mla_split_kernel(MainArgs a) {
     // scale = 2^(e-15) with amax < 2^e, so |o / scale| < 2^15 fits fp16
     const float scale = amax > 0.f ? __builtin_ldexpf(1.0f, __builtin_amdgcn_frexp_expf(amax) - 15) : 1.0f;
     const float inv_s = inv / scale;
-    uint16_t* dst = a.ws_o + rec * kRecElems;
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.ws_o + rec * kRecElems, (uint32_t)(kRecElems * 2));
 #pragma unroll
     for (int db = 0; db < 16; ++db) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const u32x2 pkd = {scale_pack_f16x2(o[db][4 * qq + 0], o[db][4 * qq + 1], inv_s),
                            scale_pack_f16x2(o[db][4 * qq + 2], o[db][4 * qq + 3], inv_s)};
-        __builtin_nontemporal_store(pkd, reinterpret_cast<u32x2*>(dst + ((db * 4 + qq) * 64 + lane) * 4));
+        buffer_store_b64_wt(pkd, prs, (unsigned)(((db * 4 + qq) * 64 + lane) * 8));
       }
     }
     if (half == 0) {
