@@ -450,6 +450,27 @@ def test_reference_rises_several_times_in_a_split(gpu_lib):
         _check(*d.results(), ref_out, ref_lse, tag=f"three rises splits={s}")
 
 
+@pytest.mark.parametrize("nats", [30.0, 100.0])
+def test_partial_last_tile_large_score(gpu_lib, nats):
+    """The sequence's last tile holds 18 keys (prefix 2,960, T = 2; the other
+    46 read as absent). A key of that tile scores `nats` above the rest: 30
+    raises the exponent reference at the tile's end, 100 sends the split to its
+    second pass. Splits 1, automatic, 3 and 47 (one tile each: the last split
+    is the partial tile alone) all match the oracle."""
+    spec = Spec("partial_last_tile", B=1, T=2, H=64, layout="contig", prefix=2960)
+    w = generate(spec, seed=33)
+    assert int(w.kv_lens[0]) % 64 == 18
+    w.q_rope[..., 0] = synth.f32_to_bf16_bits(np.ones(w.q_rope[..., 0].shape, np.float32))
+    w.k_rope[2950, 0] = synth.f32_to_bf16_bits(np.array([nats / w.scale], np.float32))[0]
+    _announce(f"partial last tile, {nats:g} nats", w)
+    ref_out, ref_lse = run_oracle(w)
+    assert ref_lse.min() > nats - 5.0
+    d = _dev(w)
+    for s in (1, 0, 3, 47):
+        d.run(num_splits=s)
+        _check(*d.results(), ref_out, ref_lse, tag=f"partial last tile {nats:g} splits={s}")
+
+
 @pytest.mark.parametrize("layout", ["contig", "sparse"])
 def test_many_splits_combine(gpu_lib, layout):
     """Groups of more than 32 splits (one sequence, or sparse tokens) combine in
