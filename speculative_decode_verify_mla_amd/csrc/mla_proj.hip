@@ -43,9 +43,12 @@ __global__ void __launch_bounds__(256) mla_proj_kernel(ProjArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int S = proj_waves(a.in_dim);
-  const int tiles_n = a.out_dim / kProjCols;
-  const int h = blockIdx.x / tiles_n;
-  const int n0 = (blockIdx.x - h * tiles_n) * kProjCols;
+  // Head fastest: workgroups are dealt to the 8 XCDs round-robin, so with a
+  // multiple of 8 heads every column slice of one head lands on one XCD, whose
+  // L2 then serves the 128-byte weight lines that neighbouring 64-byte slices
+  // share (head-major order fetched each such line from HBM twice).
+  const int h = blockIdx.x % a.heads;
+  const int n0 = (blockIdx.x / a.heads) * kProjCols;
   const int K = a.in_dim;
   const int ksteps = K / 16;
   // this wave's MFMA steps (16 input dims each)
