@@ -248,24 +248,22 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_kernel(TopkArgs a) {
 // ---------------------------------------------------------------------------
 // Several workgroups per row. With few rows, one workgroup per row leaves most
 // CUs idle, so each row is cut into `chunks` pieces, one 256-thread workgroup
-// per (row, piece), in three launches:
+// per (row, piece) for the two passes over the scores, in three launches:
 //  1. mla_topk_hist_kernel: each piece histograms the top 8 bits (digit 0) of
 //     its keys and stores the 256 counts.
 //  2. mla_topk_compact_kernel: every workgroup of a row sums the pieces'
 //     histograms and finds the digit-0 bin d0 where the count of larger keys
 //     reaches k (all reach the same answer). Keys above d0 are all selected;
-//     keys in bin d0 are candidates. Each wave walks its segment of the piece,
-//     records how many keys it has above d0, and writes its candidates
-//     (position, key), in position order, to a region of its own.
-//  3. mla_topk_place_kernel: every workgroup of a row gathers the row's
-//     candidates (usually a few percent of the row) into LDS and settles the
-//     remaining three 8-bit digits over them, which gives the threshold key T
-//     and how many keys equal to T are taken. Each (piece, wave) segment's
-//     count of keys above T is its count above d0 plus its candidates above T,
-//     its count equal to T is its candidates equal to T, so a prefix over the
-//     segments gives every wave its output offsets, and each wave places its
-//     segment's selected positions in one walk, in position order.
-// The workspace holds the histograms, the counts and the candidate regions
+//     keys in bin d0 are candidates. Each wave walks its segment of the piece
+//     and writes both kinds (position, key), in position order, to a region of
+//     its own: the row's entries, usually a few percent of it.
+//  3. mla_topk_place_kernel: one 1024-thread workgroup per row gathers the
+//     row's entries into LDS and settles the remaining three 8-bit digits over
+//     the candidates among them, which gives the threshold key T and how many
+//     keys equal to T are taken (the lowest positions). Entries above T are
+//     all taken; a block prefix over the entries, in position order, gives
+//     every taken entry its output slot. The scores are read twice in all.
+// The workspace holds the histograms, the entry counts and the entry regions
 // (room for every key of a row: a row whose keys share their top 8 bits is
 // correct, only slower). Every call rewrites what it reads.
 // ---------------------------------------------------------------------------
@@ -273,13 +271,12 @@ constexpr int kMwThreads = 256;
 constexpr int kMwWaves = kMwThreads / 64;
 constexpr int kMwRegions = 4 * kTopkMaxChunks;  // (piece, wave) candidate regions per row, at most
 static_assert(kMwRegions <= kMwThreads, "one region count per thread");
-constexpr int kCandLds = 8192;  // candidate keys of a row staged in LDS (more: read from L2)
+constexpr int kEntLds = 16384;  // entries of a row staged in LDS by the placement (more: read from L2)
 
 struct MwLayout {
   uint32_t* hist;   // [rows][chunks][256] digit-0 counts
-  int* above;       // [rows][chunks][4] keys above d0 per (piece, wave) segment
-  int* ccount;      // [rows][chunks][4] candidates per (piece, wave)
-  uint2* cand;      // [rows][chunks][4][chunk / 4] (position, key)
+  int* ccount;      // [rows][chunks][4] entries per (piece, wave) segment
+  uint2* cand;      // [rows][chunks][4][chunk / 4] entries (position, key)
 };
 __device__ __forceinline__ MwLayout mw_layout(const TopkArgs& a) {
   uint8_t* p = reinterpret_cast<uint8_t*>(a.ws);
@@ -287,8 +284,6 @@ __device__ __forceinline__ MwLayout mw_layout(const TopkArgs& a) {
   MwLayout l;
   l.hist = reinterpret_cast<uint32_t*>(p);
   p += rp * 256 * 4;
-  l.above = reinterpret_cast<int*>(p);
-  p += rp * 4 * 4;
   l.ccount = reinterpret_cast<int*>(p);
   p += rp * 4 * 4;
   l.cand = reinterpret_cast<uint2*>(p);
@@ -407,22 +402,19 @@ __global__ void __launch_bounds__(kMwThreads) mla_topk_compact_kernel(TopkArgs a
   const int64_t rp = (int64_t)row * a.chunks + piece;
   const int seg = a.chunk / kMwWaves;  // whole 256-score steps (chunk is a multiple of 1024)
   uint2* const region = l.cand + (rp * kMwWaves + wave) * seg;
-  if (kk == 0) {  // nothing selected: empty candidate regions
-    if (lane == 0) {
-      l.ccount[rp * kMwWaves + wave] = 0;
-      l.above[rp * kMwWaves + wave] = 0;
-    }
+  if (kk == 0) {  // nothing selected: empty entry regions
+    if (lane == 0) l.ccount[rp * kMwWaves + wave] = 0;
     return;
   }
   int taken;
   const uint32_t d0 = mw_settle0(a, l, row, kk, wave_tot, &s_digit, &s_above, taken);
 
-  // this wave's segment: count the keys above bin d0 (all selected) and write
-  // the candidates (keys in bin d0) in position order
+  // this wave's segment: write every key at or above bin d0 (above it: all
+  // selected; in it: candidates) as (position, key), in position order
   const float* s = a.scores + (int64_t)row * a.row_stride;
   const int p1 = min(piece * a.chunk + a.chunk, n);
   const int w0 = piece * a.chunk + wave * seg, w1 = min(w0 + seg, p1);
-  int count = 0, n_above = 0;
+  int count = 0;
   for (int base = w0; base < w1; base += kWalkBatch * 256) {
     float4 vb[kWalkBatch];
 #pragma unroll
@@ -440,9 +432,8 @@ __global__ void __launch_bounds__(kMwThreads) mla_topk_compact_kernel(TopkArgs a
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u[q] = order_key(e[q]);
-        c[q] = p + q < w1 && (u[q] >> 24) == d0;
+        c[q] = p + q < w1 && (u[q] >> 24) >= d0;
         cn += c[q];
-        n_above += (p + q < w1 && (u[q] >> 24) > d0);
       }
       const int incl = wave_incl_scan(cn);
       int at = count + incl - cn;
@@ -453,25 +444,37 @@ __global__ void __launch_bounds__(kMwThreads) mla_topk_compact_kernel(TopkArgs a
       count += __builtin_amdgcn_readlane(incl, 63);
     }
   }
-  n_above = wave_sum_i(n_above);
-  if (lane == 0) {
-    l.ccount[rp * kMwWaves + wave] = count;
-    l.above[rp * kMwWaves + wave] = n_above;
-  }
+  if (lane == 0) l.ccount[rp * kMwWaves + wave] = count;
 }
 
-__global__ void __launch_bounds__(kMwThreads) mla_topk_place_kernel(TopkArgs a) {
+// Thread t < 256 holds the count c of bin t of a 256-bin histogram (threads
+// past 255 hold 0) over the 1024 threads of the placement block. Returns the
+// bin where the count of keys in higher bins first reaches k_rem; `above` gets
+// that count. Every thread of the block must call it.
+__device__ uint32_t place_pick(int c, int k_rem, int* wave_tot, uint32_t* s_digit, int* s_above,
+                               int& above) {
+  int total;
+  const int excl = block_excl_scan(c, wave_tot, total);
+  const int hi = total - excl - c;
+  if (hi < k_rem && k_rem <= hi + c) {
+    *s_digit = (uint32_t)threadIdx.x;
+    *s_above = hi;
+  }
+  __syncthreads();
+  const uint32_t d = *s_digit;
+  above = *s_above;
+  __syncthreads();
+  return d;
+}
+
+__global__ void __launch_bounds__(kTopkThreads) mla_topk_place_kernel(TopkArgs a) {
+  __shared__ uint2 ent[kEntLds];       // the row's entries (position, key), position order
+  __shared__ int off[kMwRegions + 1];  // exclusive prefix of the regions' entry counts
   __shared__ uint32_t hist[256];
-  __shared__ int wave_tot[kMwWaves];
+  __shared__ int wave_tot[kTopkWaves];
   __shared__ uint32_t s_digit;
   __shared__ int s_above;
-  __shared__ int cnt[kMwRegions];
-  __shared__ int off[kMwRegions + 1];  // exclusive prefix of cnt over the regions
-  __shared__ uint32_t ck[kCandLds];    // the row's candidate keys, in position order
-  __shared__ int seg_gt[kMwWaves], seg_eq[kMwWaves];
-  __shared__ int rg_gt[kMwRegions], rg_eq[kMwRegions];  // per region: keys above / equal to T
-  const int row = blockIdx.x / a.chunks, piece = blockIdx.x - row * a.chunks;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x, tid = threadIdx.x;
   const int n = mw_row_len(a, row);
   const int kk = min(a.k, n);
   int32_t* out = a.indices + (int64_t)row * a.k;
@@ -481,179 +484,102 @@ __global__ void __launch_bounds__(kMwThreads) mla_topk_place_kernel(TopkArgs a) 
     const int regions = a.chunks * kMwWaves;
     const int seg = a.chunk / kMwWaves;
     const uint2* const rc = l.cand + (int64_t)row * regions * seg;
-    // Every load the prologue needs is issued at once, unconditionally (indices
-    // clamped into range, unused values masked afterwards), so one memory round
-    // trip covers the digit-0 histograms, the region counts and the first 64
-    // candidates of every region. Wave w takes region 4j + w in slot j.
-    constexpr int kSlots = kMwRegions / kMwWaves;
+    // One memory round trip: the pieces' digit-0 histograms (thread = bin) and
+    // the regions' entry counts (thread = region), loads unconditional (indices
+    // clamped into range, unused values masked afterwards).
+    const int bin = tid & 255;
     uint32_t hv[kTopkMaxChunks];
 #pragma unroll
     for (int i = 0; i < kTopkMaxChunks; ++i)
-      hv[i] = l.hist[((int64_t)row * a.chunks + min(i, a.chunks - 1)) * 256 + tid];
-    const int rt = min(tid, regions - 1);
-    const int c_ld = l.ccount[(int64_t)row * regions + rt];
-    const int ab_ld = l.above[(int64_t)row * regions + rt];
-    uint32_t v[kSlots];
-#pragma unroll
-    for (int j = 0; j < kSlots; ++j) v[j] = rc[(int64_t)min(4 * j + wave, regions - 1) * seg + lane].y;
-
+      hv[i] = l.hist[((int64_t)row * a.chunks + min(i, a.chunks - 1)) * 256 + bin];
+    const int c_ld = l.ccount[(int64_t)row * regions + min(tid, regions - 1)];
     int c0 = 0;
 #pragma unroll
     for (int i = 0; i < kTopkMaxChunks; ++i) c0 += i < a.chunks ? (int)hv[i] : 0;
     int taken;
-    const uint32_t d0 = mw_pick(c0, kk, wave_tot, &s_digit, &s_above, taken);
+    const uint32_t d0 = place_pick(tid < 256 ? c0 : 0, kk, wave_tot, &s_digit, &s_above, taken);
     int k_rem = kk - taken;  // keys still to take among the candidates (bin d0)
-    {  // region counts and their exclusive prefix (at most 128 regions: one per thread)
-      const int c = tid < regions ? c_ld : 0;
-      int total;
-      const int ex = mw_excl_scan(c, wave_tot, total);
-      if (tid < regions) {
-        cnt[tid] = c;
-        off[tid] = ex;
-        rg_gt[tid] = ab_ld;  // keys above bin d0; candidates above T are added below
-        rg_eq[tid] = 0;
-      }
-      if (tid == 0) off[regions] = total;
-      __syncthreads();
-    }
-    const int n_cand = off[regions];
-    const bool staged = n_cand <= kCandLds;
-    // Candidate key `i` of the row (regions in piece-major order = position order).
-    auto cand_key = [&](int i) -> uint32_t {
-      int lo = 0, hi = regions - 1;  // the region r with off[r] <= i < off[r + 1]
+    int n_ent;
+    const int ex = block_excl_scan(tid < regions ? c_ld : 0, wave_tot, n_ent);
+    if (tid < regions) off[tid] = ex;
+    if (tid == 0) off[regions] = n_ent;
+    __syncthreads();
+
+    // Entry i of the row: region r with off[r] <= i < off[r + 1], slot i - off[r].
+    auto global_entry = [&](int i) -> uint2 {
+      int lo = 0, hi = regions - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (off[mid] <= i) lo = mid; else hi = mid - 1;
       }
-      return rc[(int64_t)lo * seg + (i - off[lo])].y;
+      return rc[(int64_t)lo * seg + (i - off[lo])];
     };
-    // Gather the keys into LDS (staged; candidates past 64 in a region follow in
-    // a second loop), building the digit-1 histogram on the way.
-    hist[tid] = 0u;
-    __syncthreads();
-    if (staged) {
+    const bool staged = n_ent <= kEntLds;
+    if (staged) {  // up to 8 entries per thread in flight per step
+      constexpr int kStep = 8;
+      for (int i0 = 0; i0 < n_ent; i0 += kStep * kTopkThreads) {
+        uint2 v[kStep];
 #pragma unroll
-      for (int j = 0; j < kSlots; ++j) {
-        const int r = 4 * j + wave;
-        if (r < regions && lane < cnt[r]) {
-          ck[off[r] + lane] = v[j];
-          atomicAdd(&hist[(v[j] >> 16) & 0xffu], 1u);
+        for (int j = 0; j < kStep; ++j) {
+          const int i = i0 + j * kTopkThreads + tid;
+          if (i < n_ent) v[j] = global_entry(i);
+        }
+#pragma unroll
+        for (int j = 0; j < kStep; ++j) {
+          const int i = i0 + j * kTopkThreads + tid;
+          if (i < n_ent) ent[i] = v[j];
         }
       }
-      for (int r = wave; r < regions; r += kMwWaves)
-        for (int e = 64 + lane; e < cnt[r]; e += 64) {
-          const uint32_t u = rc[(int64_t)r * seg + e].y;
-          ck[off[r] + e] = u;
-          atomicAdd(&hist[(u >> 16) & 0xffu], 1u);
-        }
-    } else {
-      for (int i = tid; i < n_cand; i += kMwThreads) atomicAdd(&hist[(cand_key(i) >> 16) & 0xffu], 1u);
+      __syncthreads();
     }
-    __syncthreads();
-    auto key_at = [&](int i) -> uint32_t { return staged ? ck[i] : cand_key(i); };
+    auto entry = [&](int i) -> uint2 { return staged ? ent[i] : global_entry(i); };
 
-    // digits 1..3 over the candidates (digit 1's histogram is already built)
+    // digits 1..3 over the candidates (entries whose top byte is d0)
     uint32_t prefix = d0 << 24, pmask = 0xff000000u;
     for (int lv = 1; lv < kTopkLevels; ++lv) {
       const int shift = 24 - 8 * lv;
-      if (lv > 1) {
-        hist[tid] = 0u;
-        __syncthreads();
-        for (int i = tid; i < n_cand; i += kMwThreads) {
-          const uint32_t u = key_at(i);
-          if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 0xffu], 1u);
-        }
-        __syncthreads();
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+      for (int i = tid; i < n_ent; i += kTopkThreads) {
+        const uint32_t u = entry(i).y;
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 0xffu], 1u);
       }
+      __syncthreads();
       int above;
-      const uint32_t d = mw_pick((int)hist[tid], k_rem, wave_tot, &s_digit, &s_above, above);
+      const uint32_t d = place_pick(tid < 256 ? (int)hist[tid] : 0, k_rem, wave_tot, &s_digit, &s_above, above);
       prefix |= d << shift;
       pmask |= 0xffu << shift;
       k_rem -= above;
     }
     const uint32_t T = prefix;  // the threshold key
-    const int k_eq = k_rem;     // keys equal to T that are taken
+    const int k_eq = k_rem;     // keys equal to T that are taken (the lowest positions)
 
-    // Keys above / equal to T in every (piece, wave) segment before this wave's:
-    // a region's count above T is its keys above bin d0 (recorded by the compact
-    // launch) plus its candidates above T (summed by the wave that owns it in
-    // the slot mapping above); an exclusive prefix over the regions gives each
-    // wave of this piece its starting offsets.
-    {
-      const int last = (piece + 1) * kMwWaves;  // regions up to this piece's
-      for (int j = 0; j < kSlots; ++j) {
-        const int r = 4 * j + wave;
-        if (r >= last) break;  // uniform per wave
-        int g = 0, q = 0;
-        for (int e0 = 0; e0 < cnt[r]; e0 += 64) {
-          const bool in = e0 + lane < cnt[r];
-          const uint32_t u = in ? key_at(off[r] + e0 + lane) : 0u;
-          g += __popcll(__ballot(in && u > T));
-          q += __popcll(__ballot(in && u == T));
-        }
-        if (lane == 0) {
-          rg_gt[r] += g;
-          rg_eq[r] = q;
-        }
-      }
-      __syncthreads();
-      const int gt = tid < last ? rg_gt[tid] : 0, eq = tid < last ? rg_eq[tid] : 0;
-      int tg, te;
-      const int xg = mw_excl_scan(gt, wave_tot, tg);
-      const int xe = mw_excl_scan(eq, wave_tot, te);
-      if (tid >= piece * kMwWaves && tid < last) {
-        seg_gt[tid - piece * kMwWaves] = xg;
-        seg_eq[tid - piece * kMwWaves] = xe;
-      }
-      __syncthreads();
+    // Every entry above T is taken, and the first k_eq entries equal to T: each
+    // thread counts its contiguous run of entries, two block prefixes give its
+    // starting output slot and equal-rank, and it places its run in order.
+    const int per = (n_ent + kTopkThreads - 1) / kTopkThreads;
+    const int e0 = min(tid * per, n_ent), e1 = min(e0 + per, n_ent);
+    int gt = 0, eq = 0;
+    for (int i = e0; i < e1; ++i) {
+      const uint32_t u = entry(i).y;
+      gt += u > T;
+      eq += u == T;
     }
-
-    // Each wave walks its segment of the piece (whole 256-score steps) once,
-    // placing positions by wave-local prefix sums from its starting offsets.
-    const float* s = a.scores + (int64_t)row * a.row_stride;
-    const int p1 = min(piece * a.chunk + a.chunk, n);
-    const int w0 = piece * a.chunk + wave * seg, w1 = min(w0 + seg, p1);
-    int G = seg_gt[wave], E = seg_eq[wave];
-    for (int base = w0; base < w1; base += kWalkBatch * 256) {
-      float4 vb[kWalkBatch];
-#pragma unroll
-      for (int j = 0; j < kWalkBatch; ++j) {
-        const int p = base + 256 * j + 4 * lane;
-        vb[j] = p < w1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int j = 0; j < kWalkBatch; ++j) {
-        const int p = base + 256 * j + 4 * lane;
-        const float e[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
-        bool gt[4], eq[4];
-        int cg = 0, ce = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t u = order_key(e[q]);
-          gt[q] = p + q < w1 && u > T;
-          eq[q] = p + q < w1 && u == T;
-          cg += gt[q];
-          ce += eq[q];
-        }
-        const int packed = cg | (ce << 16);
-        const int incl = wave_incl_scan(packed);
-        const int step_tot = __builtin_amdgcn_readlane(incl, 63);
-        int g = G + ((incl - packed) & 0xffff), eqb = E + ((incl - packed) >> 16);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bool take = gt[q] || (eq[q] && eqb < k_eq);
-          const int pos = g + min(eqb, k_eq);
-          if (take && pos < kk) out[pos] = p + q;
-          g += gt[q];
-          eqb += eq[q];
-        }
-        G += step_tot & 0xffff;
-        E += step_tot >> 16;
+    int tg, te;
+    int G = block_excl_scan(gt, wave_tot, tg);
+    int E = block_excl_scan(eq, wave_tot, te);
+    for (int i = e0; i < e1; ++i) {
+      const uint2 v = entry(i);
+      if (v.y > T) {
+        out[G + min(E, k_eq)] = (int32_t)v.x;
+        ++G;
+      } else if (v.y == T) {
+        if (E < k_eq) out[G + E] = (int32_t)v.x;
+        ++E;
       }
     }
   }
-  if (piece == 0)
-    for (int i = kk + tid; i < a.k; i += kMwThreads) out[i] = -1;
+  for (int i = kk + tid; i < a.k; i += kTopkThreads) out[i] = -1;
 }
 
 }  // namespace
@@ -670,7 +596,7 @@ hipError_t launch_topk_kernel(const TopkArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(mla_topk_compact_kernel, dim3(grid), dim3(kMwThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_topk_place_kernel, dim3(grid), dim3(kMwThreads), 0, stream, a);
+  hipLaunchKernelGGL(mla_topk_place_kernel, dim3(a.rows), dim3(kTopkThreads), 0, stream, a);
   return hipGetLastError();
 }
 
