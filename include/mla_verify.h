@@ -264,7 +264,7 @@ int mla_select_topk(int32_t rows, int32_t row_len, int64_t row_stride, int32_t k
 
 /* Workspace bytes for mla_select_topk's several-workgroup path on any device
  * (0 when rows are never split: row_len <= 4096 or invalid arguments):
- * rows x (up to 32 pieces x 1,040 + (row_len + 1,024 x pieces) x 8). */
+ * rows x (up to 32 pieces x 1,056 + (row_len + 1,024 x pieces) x 8). */
 size_t mla_select_topk_workspace_bytes(int32_t rows, int32_t row_len);
 
 /* Static description of an error code (never NULL). */

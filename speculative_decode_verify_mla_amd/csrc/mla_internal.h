@@ -113,9 +113,10 @@ constexpr int kTopkMaxChunks = 32;   // pieces per row
 constexpr int kTopkMinChunk = 4096;  // scores per piece, at least
 constexpr int kTopkLevels = 4;       // 8-bit digits of the 32-bit order key
 // Workspace bytes of the several-workgroup path for `rows` rows cut into
-// `chunks` pieces of `chunk` scores: per piece a 256-bin histogram and an
-// entry count per wave segment, and entry room for every score (8 bytes each).
-constexpr int64_t topk_piece_bytes = 256 * 4 + 16;
+// `chunks` pieces of `chunk` scores: per piece a 256-bin histogram, an entry
+// count per wave segment and a 16-byte digit-0 record, and entry room for
+// every score (8 bytes each).
+constexpr int64_t topk_piece_bytes = 256 * 4 + 16 + 16;
 constexpr int64_t topk_workspace_bytes(int64_t rows, int64_t chunks, int64_t chunk) {
   return rows * chunks * topk_piece_bytes + rows * chunks * chunk * 8;
 }

@@ -276,6 +276,7 @@ constexpr int kEntLds = 16384;  // entries of a row staged in LDS by the placeme
 struct MwLayout {
   uint32_t* hist;   // [rows][chunks][256] digit-0 counts
   int* ccount;      // [rows][chunks][4] entries per (piece, wave) segment
+  int4* settle;     // [rows][chunks] digit-0 bin d0 and the count above it (x, y)
   uint2* cand;      // [rows][chunks][4][chunk / 4] entries (position, key)
 };
 __device__ __forceinline__ MwLayout mw_layout(const TopkArgs& a) {
@@ -286,6 +287,8 @@ __device__ __forceinline__ MwLayout mw_layout(const TopkArgs& a) {
   p += rp * 256 * 4;
   l.ccount = reinterpret_cast<int*>(p);
   p += rp * 4 * 4;
+  l.settle = reinterpret_cast<int4*>(p);
+  p += rp * 16;
   l.cand = reinterpret_cast<uint2*>(p);
   return l;
 }
@@ -408,6 +411,7 @@ __global__ void __launch_bounds__(kMwThreads) mla_topk_compact_kernel(TopkArgs a
   }
   int taken;
   const uint32_t d0 = mw_settle0(a, l, row, kk, wave_tot, &s_digit, &s_above, taken);
+  if (tid == 0) l.settle[rp] = make_int4((int)d0, taken, 0, 0);
 
   // this wave's segment: write every key at or above bin d0 (above it: all
   // selected; in it: candidates) as (position, key), in position order
@@ -470,6 +474,7 @@ __device__ uint32_t place_pick(int c, int k_rem, int* wave_tot, uint32_t* s_digi
 __global__ void __launch_bounds__(kTopkThreads) mla_topk_place_kernel(TopkArgs a) {
   __shared__ uint2 ent[kEntLds];       // the row's entries (position, key), position order
   __shared__ int off[kMwRegions + 1];  // exclusive prefix of the regions' entry counts
+  __shared__ int cnt[kMwRegions];
   __shared__ uint32_t hist[256];
   __shared__ int wave_tot[kTopkWaves];
   __shared__ uint32_t s_digit;
@@ -484,24 +489,18 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_place_kernel(TopkArgs a
     const int regions = a.chunks * kMwWaves;
     const int seg = a.chunk / kMwWaves;
     const uint2* const rc = l.cand + (int64_t)row * regions * seg;
-    // One memory round trip: the pieces' digit-0 histograms (thread = bin) and
-    // the regions' entry counts (thread = region), loads unconditional (indices
-    // clamped into range, unused values masked afterwards).
-    const int bin = tid & 255;
-    uint32_t hv[kTopkMaxChunks];
-#pragma unroll
-    for (int i = 0; i < kTopkMaxChunks; ++i)
-      hv[i] = l.hist[((int64_t)row * a.chunks + min(i, a.chunks - 1)) * 256 + bin];
+    // One memory round trip: the digit-0 settlement the compaction recorded
+    // (piece 0's copy) and the regions' entry counts (thread = region).
+    const int4 st0 = l.settle[(int64_t)row * a.chunks];
     const int c_ld = l.ccount[(int64_t)row * regions + min(tid, regions - 1)];
-    int c0 = 0;
-#pragma unroll
-    for (int i = 0; i < kTopkMaxChunks; ++i) c0 += i < a.chunks ? (int)hv[i] : 0;
-    int taken;
-    const uint32_t d0 = place_pick(tid < 256 ? c0 : 0, kk, wave_tot, &s_digit, &s_above, taken);
-    int k_rem = kk - taken;  // keys still to take among the candidates (bin d0)
+    const uint32_t d0 = (uint32_t)st0.x;
+    int k_rem = kk - st0.y;  // keys still to take among the candidates (bin d0)
     int n_ent;
     const int ex = block_excl_scan(tid < regions ? c_ld : 0, wave_tot, n_ent);
-    if (tid < regions) off[tid] = ex;
+    if (tid < regions) {
+      off[tid] = ex;
+      cnt[tid] = c_ld;
+    }
     if (tid == 0) off[regions] = n_ent;
     __syncthreads();
 
@@ -515,21 +514,24 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_place_kernel(TopkArgs a
       return rc[(int64_t)lo * seg + (i - off[lo])];
     };
     const bool staged = n_ent <= kEntLds;
-    if (staged) {  // up to 8 entries per thread in flight per step
-      constexpr int kStep = 8;
-      for (int i0 = 0; i0 < n_ent; i0 += kStep * kTopkThreads) {
-        uint2 v[kStep];
+    if (staged) {
+      // wave w copies regions w, w + 16, ... (all of their first 64 entries in
+      // flight at once; longer regions continue in a second loop)
+      constexpr int kSlots = kMwRegions / kTopkWaves;
+      const int wave = tid >> 6, lane = tid & 63;
+      uint2 v[kSlots];
 #pragma unroll
-        for (int j = 0; j < kStep; ++j) {
-          const int i = i0 + j * kTopkThreads + tid;
-          if (i < n_ent) v[j] = global_entry(i);
-        }
-#pragma unroll
-        for (int j = 0; j < kStep; ++j) {
-          const int i = i0 + j * kTopkThreads + tid;
-          if (i < n_ent) ent[i] = v[j];
-        }
+      for (int j = 0; j < kSlots; ++j) {
+        const int r = wave + kTopkWaves * j;
+        if (r < regions && lane < cnt[r]) v[j] = rc[(int64_t)r * seg + lane];
       }
+#pragma unroll
+      for (int j = 0; j < kSlots; ++j) {
+        const int r = wave + kTopkWaves * j;
+        if (r < regions && lane < cnt[r]) ent[off[r] + lane] = v[j];
+      }
+      for (int r = wave; r < regions; r += kTopkWaves)
+        for (int e = 64 + lane; e < cnt[r]; e += 64) ent[off[r] + e] = rc[(int64_t)r * seg + e];
       __syncthreads();
     }
     auto entry = [&](int i) -> uint2 { return staged ? ent[i] : global_entry(i); };

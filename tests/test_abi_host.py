@@ -272,11 +272,12 @@ def test_topk_and_projection_invalid_arguments(lib):
 
 def test_topk_workspace_bytes(lib):
     w = lib.mla_select_topk_workspace_bytes
-    # at most 32 pieces: per piece 256 bins + 4 counts (4 B each), and entry
-    # room for every score plus one 1024-score step per piece (8 B each)
-    assert w(32, 131072) == 32 * 32 * 1040 + 32 * (131072 + 32 * 1024) * 8
+    # at most 32 pieces: per piece 256 bins + 4 counts (4 B each) and a 16-byte
+    # digit-0 record, and entry room for every score plus one 1024-score step
+    # per piece (8 B each)
+    assert w(32, 131072) == 32 * 32 * 1056 + 32 * (131072 + 32 * 1024) * 8
     assert w(1, 4096) == 0          # one piece: no workspace
-    assert w(3, 9000) == 3 * 3 * 1040 + 3 * (9000 + 3 * 1024) * 8
+    assert w(3, 9000) == 3 * 3 * 1056 + 3 * (9000 + 3 * 1024) * 8
     assert w(0, 100) == 0 and w(2, 0) == 0
 
 
