@@ -111,7 +111,6 @@ struct TopkArgs {
 };
 constexpr int kTopkMaxChunks = 32;   // pieces per row
 constexpr int kTopkMinChunk = 4096;  // scores per piece, at least
-constexpr int kTopkLevels = 4;       // 8-bit digits of the 32-bit order key
 // Workspace bytes of the several-workgroup path for `rows` rows cut into
 // `chunks` pieces of `chunk` scores: per piece a 256-bin histogram, an entry
 // count per wave segment and a 16-byte digit-0 record, and entry room for

@@ -258,8 +258,8 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_kernel(TopkArgs a) {
 //     and writes both kinds (position, key), in position order, to a region of
 //     its own: the row's entries, usually a few percent of it.
 //  3. mla_topk_place_kernel: one 1024-thread workgroup per row gathers the
-//     row's entries into LDS and settles the remaining three 8-bit digits over
-//     the candidates among them, which gives the threshold key T and how many
+//     row's entries into LDS and settles the remaining 24 bits (two 12-bit
+//     digits) over the candidates among them, which gives the threshold key T and how many
 //     keys equal to T are taken (the lowest positions). Entries above T are
 //     all taken; a block prefix over the entries, in position order, gives
 //     every taken entry its output slot. The scores are read twice in all.
@@ -451,31 +451,11 @@ __global__ void __launch_bounds__(kMwThreads) mla_topk_compact_kernel(TopkArgs a
   if (lane == 0) l.ccount[rp * kMwWaves + wave] = count;
 }
 
-// Thread t < 256 holds the count c of bin t of a 256-bin histogram (threads
-// past 255 hold 0) over the 1024 threads of the placement block. Returns the
-// bin where the count of keys in higher bins first reaches k_rem; `above` gets
-// that count. Every thread of the block must call it.
-__device__ uint32_t place_pick(int c, int k_rem, int* wave_tot, uint32_t* s_digit, int* s_above,
-                               int& above) {
-  int total;
-  const int excl = block_excl_scan(c, wave_tot, total);
-  const int hi = total - excl - c;
-  if (hi < k_rem && k_rem <= hi + c) {
-    *s_digit = (uint32_t)threadIdx.x;
-    *s_above = hi;
-  }
-  __syncthreads();
-  const uint32_t d = *s_digit;
-  above = *s_above;
-  __syncthreads();
-  return d;
-}
-
 __global__ void __launch_bounds__(kTopkThreads) mla_topk_place_kernel(TopkArgs a) {
   __shared__ uint2 ent[kEntLds];       // the row's entries (position, key), position order
   __shared__ int off[kMwRegions + 1];  // exclusive prefix of the regions' entry counts
   __shared__ int cnt[kMwRegions];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[4 * kTopkThreads];
   __shared__ int wave_tot[kTopkWaves];
   __shared__ uint32_t s_digit;
   __shared__ int s_above;
@@ -536,21 +516,41 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_place_kernel(TopkArgs a
     }
     auto entry = [&](int i) -> uint2 { return staged ? ent[i] : global_entry(i); };
 
-    // digits 1..3 over the candidates (entries whose top byte is d0)
+    // the low 24 bits over the candidates (entries whose top byte is d0), as
+    // two 12-bit digits: thread t holds bins 4t .. 4t+3 of a 4096-bin histogram
     uint32_t prefix = d0 << 24, pmask = 0xff000000u;
-    for (int lv = 1; lv < kTopkLevels; ++lv) {
-      const int shift = 24 - 8 * lv;
-      if (tid < 256) hist[tid] = 0u;
+    for (int shift = 12; shift >= 0; shift -= 12) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hist[4 * tid + j] = 0u;
       __syncthreads();
       for (int i = tid; i < n_ent; i += kTopkThreads) {
         const uint32_t u = entry(i).y;
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 0xffu], 1u);
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 0xfffu], 1u);
       }
       __syncthreads();
-      int above;
-      const uint32_t d = place_pick(tid < 256 ? (int)hist[tid] : 0, k_rem, wave_tot, &s_digit, &s_above, above);
+      uint32_t h4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h4[j] = hist[4 * tid + j];
+      const int c4 = (int)(h4[0] + h4[1] + h4[2] + h4[3]);
+      int total;
+      const int excl = block_excl_scan(c4, wave_tot, total);
+      int hi = total - excl - c4;  // keys in bins above this thread's four
+      if (hi < k_rem && k_rem <= hi + c4) {  // exactly one thread of the block
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (hi < k_rem && k_rem <= hi + (int)h4[j]) {
+            s_digit = (uint32_t)(4 * tid + j);
+            s_above = hi;
+          }
+          hi += (int)h4[j];
+        }
+      }
+      __syncthreads();
+      const uint32_t d = s_digit;
+      const int above = s_above;
+      __syncthreads();
       prefix |= d << shift;
-      pmask |= 0xffu << shift;
+      pmask |= 0xfffu << shift;
       k_rem -= above;
     }
     const uint32_t T = prefix;  // the threshold key
