@@ -409,23 +409,29 @@ __global__ void __launch_bounds__(kMwThreads) mla_topk_compact_kernel(TopkArgs a
     if (lane == 0) l.ccount[rp * kMwWaves + wave] = 0;
     return;
   }
-  int taken;
-  const uint32_t d0 = mw_settle0(a, l, row, kk, wave_tot, &s_digit, &s_above, taken);
-  if (tid == 0) l.settle[rp] = make_int4((int)d0, taken, 0, 0);
-
   // this wave's segment: write every key at or above bin d0 (above it: all
-  // selected; in it: candidates) as (position, key), in position order
+  // selected; in it: candidates) as (position, key), in position order. The
+  // first batch of scores is loaded before d0 is settled, so its round trip
+  // overlaps the one of the pieces' histograms.
   const float* s = a.scores + (int64_t)row * a.row_stride;
   const int p1 = min(piece * a.chunk + a.chunk, n);
   const int w0 = piece * a.chunk + wave * seg, w1 = min(w0 + seg, p1);
-  int count = 0;
-  for (int base = w0; base < w1; base += kWalkBatch * 256) {
-    float4 vb[kWalkBatch];
+  float4 vb[kWalkBatch];
+  auto load_batch = [&](int base) {
 #pragma unroll
     for (int j = 0; j < kWalkBatch; ++j) {
       const int p = base + 256 * j + 4 * lane;
       vb[j] = p < w1 ? load4(s, p) : float4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+  load_batch(w0);
+  int taken;
+  const uint32_t d0 = mw_settle0(a, l, row, kk, wave_tot, &s_digit, &s_above, taken);
+  if (tid == 0) l.settle[rp] = make_int4((int)d0, taken, 0, 0);
+
+  int count = 0;
+  for (int base = w0; base < w1; base += kWalkBatch * 256) {
+    if (base != w0) load_batch(base);
 #pragma unroll
     for (int j = 0; j < kWalkBatch; ++j) {
       const int p = base + 256 * j + 4 * lane;
