@@ -476,7 +476,15 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_place_kernel(TopkArgs a
     const int seg = a.chunk / kMwWaves;
     const uint2* const rc = l.cand + (int64_t)row * regions * seg;
     // One memory round trip: the digit-0 settlement the compaction recorded
-    // (piece 0's copy) and the regions' entry counts (thread = region).
+    // (piece 0's copy), the regions' entry counts (thread = region) and the
+    // first 64 entry slots of every region (wave w: regions w, w + 16, ...;
+    // loaded before the counts are known, slots past a count unused).
+    constexpr int kSlots = kMwRegions / kTopkWaves;
+    const int wave = tid >> 6, lane = tid & 63;
+    uint2 v[kSlots];
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j)
+      v[j] = rc[(int64_t)min(wave + kTopkWaves * j, regions - 1) * seg + lane];
     const int4 st0 = l.settle[(int64_t)row * a.chunks];
     const int c_ld = l.ccount[(int64_t)row * regions + min(tid, regions - 1)];
     const uint32_t d0 = (uint32_t)st0.x;
@@ -500,17 +508,7 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_place_kernel(TopkArgs a
       return rc[(int64_t)lo * seg + (i - off[lo])];
     };
     const bool staged = n_ent <= kEntLds;
-    if (staged) {
-      // wave w copies regions w, w + 16, ... (all of their first 64 entries in
-      // flight at once; longer regions continue in a second loop)
-      constexpr int kSlots = kMwRegions / kTopkWaves;
-      const int wave = tid >> 6, lane = tid & 63;
-      uint2 v[kSlots];
-#pragma unroll
-      for (int j = 0; j < kSlots; ++j) {
-        const int r = wave + kTopkWaves * j;
-        if (r < regions && lane < cnt[r]) v[j] = rc[(int64_t)r * seg + lane];
-      }
+    if (staged) {  // (longer regions continue in a second loop)
 #pragma unroll
       for (int j = 0; j < kSlots; ++j) {
         const int r = wave + kTopkWaves * j;
@@ -573,9 +571,15 @@ __global__ void __launch_bounds__(kTopkThreads) mla_topk_place_kernel(TopkArgs a
       gt += u > T;
       eq += u == T;
     }
-    int tg, te;
-    int G = block_excl_scan(gt, wave_tot, tg);
-    int E = block_excl_scan(eq, wave_tot, te);
+    int G, E, tg, te;
+    if (staged) {  // both counts below 2^16: one prefix of the packed pair
+      const int gq = block_excl_scan(gt | (eq << 16), wave_tot, tg);
+      G = gq & 0xffff;
+      E = gq >> 16;
+    } else {
+      G = block_excl_scan(gt, wave_tot, tg);
+      E = block_excl_scan(eq, wave_tot, te);
+    }
     for (int i = e0; i < e1; ++i) {
       const uint2 v = entry(i);
       if (v.y > T) {
