@@ -44,6 +44,10 @@ CASES = [
     ("ragged_long", lambda r: r.standard_normal((4, 50000)), 3000, [50000, 8191, 4097, 0]),
     ("k_over_n_long", lambda r: r.standard_normal((2, 9000)), 12000, None),
     ("low_bits_long", lambda r: 1.0 + r.integers(0, 5, size=(2, 30000)) * 2.0 ** -22, 10001, None),
+    # the selected keys packed into the first ~3 wave segments of each row:
+    # ~1,000 entries per segment region, all of them staged in LDS
+    ("clustered_long", lambda r: np.concatenate([10.0 + r.random((2, 3000)),
+                                                 r.standard_normal((2, 62536))], axis=1), 2000, None),
 ]
 
 
