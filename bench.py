@@ -47,6 +47,20 @@ def kernel_source_hash() -> str:
 
 
 # ---------------------------------------------------------------------------
+# The naive kernel the pages measure against ("The Shared Memory Ceiling",
+# section "The Guard: Turning a Limitation into a Demonstration"): it holds the
+# fp32 query row (Dl + Dr) and the fp32 score row (kv_len) in on-chip memory,
+# and its launch is skipped ("n/a") when that exceeds the memory a block gets.
+# ---------------------------------------------------------------------------
+def naive_score_row_bytes(kv_len: int, dl: int = 512, dr: int = 64) -> int:
+    return (dl + dr + int(kv_len)) * 4
+
+
+def naive_row_fits(kv_len: int, limit_bytes: int) -> bool:
+    return naive_score_row_bytes(kv_len) <= limit_bytes
+
+
+# ---------------------------------------------------------------------------
 # Algorithmic work of one call (each visible KV row counted once per sequence)
 # ---------------------------------------------------------------------------
 def work_model(w):
@@ -694,13 +708,13 @@ def bench_sweep(args, dev):
             e1.record(vc.stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) / args.steps * 1e3
-            naive = (512 + 64 + int(w.kv_lens[0])) * 4
+            naive = naive_score_row_bytes(int(w.kv_lens[0]))
             r = {"T": T, "prefix": L, "us_per_call": round(us, 3),
                  "hbm_GBps": round(wm["total_bytes"] / (us * 1e-6) / 1e9, 1),
                  "TFLOPs": round(wm["flops"] / (us * 1e-6) / 1e12, 1),
                  "splits": int(vc.info.num_splits), "workgroups": vc.workgroups,
                  "naive_score_row_bytes": naive,
-                 "naive_row_in_lds": "fits" if naive <= lds else "n/a"}
+                 "naive_row_in_lds": "fits" if naive_row_fits(int(w.kv_lens[0]), lds) else "n/a"}
             log(f"sweep T={T:2d} prefix={L:6d}: {us:9.2f} us  {r['hbm_GBps']:7.1f} GB/s  "
                 f"{r['TFLOPs']:7.1f} TFLOP/s  splits={r['splits']}  naive row {naive} B: "
                 f"{r['naive_row_in_lds']}")

@@ -1,5 +1,6 @@
 """Seeded generator checks (CPU): structure, reproducibility and bf16 encoding."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -100,3 +101,23 @@ def test_poison_rows_are_nan_and_unread_region():
         for p in range(int(w.kv_lens[b])):
             r = int(w.page_table[b, p // 64]) * 64 + p % 64
             assert not np.isnan(vals[r]).any()
+
+
+def test_naive_guard_matches_the_pages():
+    """bench.py's naive-kernel column ("fits" / "n/a" in the prefix sweep) uses the
+    pages' guard arithmetic: tests/golden/naive_score_row.txt holds the printed
+    formula's constants and the values they give."""
+    import bench
+    path = os.path.join(os.path.dirname(__file__), "golden", "naive_score_row.txt")
+    g = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split()
+            g[k] = int(v)
+    assert bench.naive_score_row_bytes(0) == (g["dl"] + g["dr"]) * 4
+    assert 65536 * 4 == g["score_row_only_bytes_at_65536"]
+    assert bench.naive_row_fits(g["largest_kv_len_within_guard"], g["guard_bytes"])
+    assert not bench.naive_row_fits(g["first_kv_len_over_guard"], g["guard_bytes"])
+    # on MI355X (160 KiB of LDS per CU) the same row fits up to 40,384 keys
+    assert bench.naive_row_fits(40384, 163840) and not bench.naive_row_fits(40385, 163840)
