@@ -505,3 +505,28 @@ def test_many_splits_combine(gpu_lib, layout):
         for splits in (33, 47):
             d.run(num_splits=splits)
             _check(*d.results(), *ref, tag=f"sparse many splits s={splits}")
+
+
+@pytest.mark.parametrize("layout", ["contig", "batch", "sparse"])
+def test_combine_batches_of_17_to_24_splits(gpu_lib, layout):
+    """The one-stage combine's 24-split body (groups of 17..24 splits) for all
+    three record layouts: one sequence, a batch (records found through the
+    split kernel's map) and sparse tokens."""
+    if layout == "contig":
+        w = generate(Spec("c24_one", B=1, T=3, H=64, layout="contig", prefix=1400), seed=34)
+        splits = (17, 20, 22)
+    elif layout == "batch":
+        # a requested count cuts every sequence into chunks of one tile: 22 and 12 splits
+        w = generate(Spec("c24_batch", B=2, T=3, H=40, layout="contig", prefix=[1400, 700]), seed=35)
+        splits = (22,)
+    else:
+        # 22 index tiles per token, one per split
+        w = generate(Spec("c24_sparse", B=2, T=2, H=64, layout="sparse", cache_len=4000, topk=1408),
+                     seed=36)
+        splits = (22,)
+    _announce(f"combine of 17..24 splits, {layout}", w)
+    ref = run_oracle(w)
+    d = _dev(w)
+    for s in splits:
+        d.run(num_splits=s)
+        _check(*d.results(), *ref, tag=f"{layout} splits={s}")
