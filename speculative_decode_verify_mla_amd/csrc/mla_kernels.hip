@@ -1156,38 +1156,38 @@ __device__ __forceinline__ void group_records(const MainArgs& a, int group, int 
 
 // Combine for groups of more than 32 splits (sparse calls and single
 // sequences, whose split count is planned on the host), in one launch: block =
-// (wave record, 8-dim group g = 4 db + qq), i.e. 32 rows x 8 dims, the 512
-// contiguous bytes of every split's record that hold them; 512 threads = 8
-// split groups x 64 lanes (row l32, dims 4h .. 4h+3). Each thread issues the
-// loads of its splits' partials (sg, sg + 8, ...; at most KPT) before anything
-// else, phase 1 turns the statistics (16 split lanes per row) into weights in
-// LDS meanwhile, each split group accumulates its splits, and the 8 sums meet in
-// LDS: one memory round trip in all, where the two-stage combine took two
-// launches with two round trips each and measured slower (a T=1 decode over a
-// 65,536-key prefix, 205 splits: 39.5 against 37.6 us per call).
+// (wave record, 4-dim group g4 = 2 g + h, g = 4 db + qq), i.e. 32 rows x 4
+// dims, the 256 contiguous bytes of every split's record that hold them; 512
+// threads = 16 split groups x 32 rows. Each thread issues the loads of its
+// splits' partials (sg, sg + 16, ...; at most KPT) and statistics before
+// anything else, phase 1 turns the statistics into weights in LDS meanwhile,
+// each split group accumulates its splits, and the 16 sums meet in LDS: one
+// memory round trip in all. (A T=1 decode over a 65,536-key prefix, 205
+// splits: 8-dim blocks of 8 split groups took 7.8 us, these 6.5; two launches
+// with two round trips each took the call to 39.5 us against 37.6.)
 constexpr int kWideThreads = 512;
-constexpr int kWideGroups = kWideThreads / 64;  // split groups
+constexpr int kWideGroups = kWideThreads / 32;  // split groups of 32 rows
 template <int KPT>
 __device__ __forceinline__ void combine_wide(const MainArgs& a, float (*wts)[kMaxSplits + 1],
-                                             float (*red)[16][kRowsPerWave], f32x4 (*gsum)[64],
-                                             float* row_lse, float* row_inv, int g, int rb, int group,
+                                             float (*red)[16][kRowsPerWave], f32x4 (*gsum)[32],
+                                             float* row_lse, float* row_inv, int g4, int rb, int group,
                                              int wave, int n_plan, int n_active, int64_t rec0,
                                              int64_t rec_stride) {
   const int t = threadIdx.x;
-  const int sg = t >> 6, lane = t & 63, half = lane >> 5, l32 = lane & 31;
-  const uint16_t* o_p = a.ws_o + rec0 * kRecElems + (g * 64 + lane) * 4;
+  const int sg = t >> 5, l32 = t & 31;
+  const int g = g4 >> 1, half = g4 & 1;
+  const uint16_t* o_p = a.ws_o + rec0 * kRecElems + (g * 64 + half * 32 + l32) * 4;
   const int64_t o_step = rec_stride * kRecElems;
   uint2 raw[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     raw[j] = *reinterpret_cast<const uint2*>(o_p + min(sg + kWideGroups * j, n_plan - 1) * o_step);
-  // the statistics of splits sl, sl + 16, ... (phase 1: thread = row r x split
-  // lane sl; at most KPT / 2 each), read once (loading them before the partials
+  // the same splits' statistics, read once (loading them before the partials
   // measured slower)
-  const int r = t & 31, sl = t >> 5;  // 16 split lanes per row
+  const int r = l32, sl = sg;
   const int64_t st_step = rec_stride * (kRecRowStats * kRowsPerWave);
   const float* st = a.ws_lse + rec0 * (kRecRowStats * kRowsPerWave) + r;
-  constexpr int KST = KPT / 2;
+  constexpr int KST = KPT;
   float h_le[KST], h_lq[KST], h_sc[KST];
 #pragma unroll
   for (int i = 0; i < KST; ++i) {
@@ -1255,11 +1255,11 @@ __device__ __forceinline__ void combine_wide(const MainArgs& a, float (*wts)[kMa
       acc[3] += w * (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[j].y >> 16));
     }
   }
-  if (sg > 0) gsum[sg - 1][lane] = acc;
+  if (sg > 0) gsum[sg - 1][l32] = acc;
   __syncthreads();
   if (sg > 0) return;
 #pragma unroll
-  for (int j = 0; j < kWideGroups - 1; ++j) acc += gsum[j][lane];
+  for (int j = 0; j < kWideGroups - 1; ++j) acc += gsum[j][l32];
   const int row = rb * kRowsPerBlock + wave * kRowsPerWave + l32;
   if (row >= a.rows_per_group) return;
   const float inv = row_inv[l32];
@@ -1269,7 +1269,7 @@ __device__ __forceinline__ void combine_wide(const MainArgs& a, float (*wts)[kMa
   pkd.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   pkd.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
   *reinterpret_cast<uint2*>(a.out + qrow * kDL + d) = pkd;
-  if (g == 0 && half == 0) a.lse[qrow] = row_lse[l32];
+  if (g4 == 0) a.lse[qrow] = row_lse[l32];
 }
 
 template <int MODE>
@@ -1277,12 +1277,12 @@ __global__ void __launch_bounds__(kWideThreads) mla_combine_wide_kernel(MainArgs
   constexpr bool kSparseMode = MODE == kSparse || MODE == kSparsePaged;
   __shared__ float wts[kRowsPerWave][kMaxSplits + 1];  // unnormalised weight x fp16 scale
   __shared__ float red[2][16][kRowsPerWave];
-  __shared__ f32x4 gsum[kWideGroups - 1][64];
+  __shared__ f32x4 gsum[kWideGroups - 1][32];
   __shared__ float row_lse[kRowsPerWave];
   __shared__ float row_inv[kRowsPerWave];
   const int bid = blockIdx.x;
-  const int g = bid & 63;
-  const int wrec = bid >> 6;
+  const int g4 = bid & 127;
+  const int wrec = bid >> 7;
   const int wave = wrec & 3;
   const int rbg = wrec >> 2;
   const int rb = rbg % a.row_blocks;
@@ -1291,13 +1291,13 @@ __global__ void __launch_bounds__(kWideThreads) mla_combine_wide_kernel(MainArgs
   int n_plan, n_active;
   int64_t rec0, rec_stride;
   group_records<kSparseMode>(a, group, rb, wave, n_plan, n_active, rec0, rec_stride);
-  static_assert(kWideGroups * 32 >= kMaxSplits, "one batch of loads covers every split");
-  if (n_plan <= kWideGroups * 8)
-    combine_wide<8>(a, wts, red, gsum, row_lse, row_inv, g, rb, group, wave, n_plan, n_active, rec0, rec_stride);
-  else if (n_plan <= kWideGroups * 16)
-    combine_wide<16>(a, wts, red, gsum, row_lse, row_inv, g, rb, group, wave, n_plan, n_active, rec0, rec_stride);
+  static_assert(kWideGroups * 16 >= kMaxSplits, "one batch of loads covers every split");
+  if (n_plan <= kWideGroups * 4)
+    combine_wide<4>(a, wts, red, gsum, row_lse, row_inv, g4, rb, group, wave, n_plan, n_active, rec0, rec_stride);
+  else if (n_plan <= kWideGroups * 8)
+    combine_wide<8>(a, wts, red, gsum, row_lse, row_inv, g4, rb, group, wave, n_plan, n_active, rec0, rec_stride);
   else
-    combine_wide<32>(a, wts, red, gsum, row_lse, row_inv, g, rb, group, wave, n_plan, n_active, rec0, rec_stride);
+    combine_wide<16>(a, wts, red, gsum, row_lse, row_inv, g4, rb, group, wave, n_plan, n_active, rec0, rec_stride);
 }
 
 template <int MODE>
@@ -1351,7 +1351,7 @@ template <int MODE>
 static hipError_t launch_combine(const MainArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)a.num_groups * (unsigned)a.row_blocks * kWaves * 16u;
   if (a.wide_combine) {
-    hipLaunchKernelGGL(mla_combine_wide_kernel<MODE>, dim3(grid * 4u), dim3(kWideThreads), 0, s, a);
+    hipLaunchKernelGGL(mla_combine_wide_kernel<MODE>, dim3(grid * 8u), dim3(kWideThreads), 0, s, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(mla_combine_kernel<MODE>, dim3(grid), dim3(256), 0, s, a);
